@@ -1,0 +1,18 @@
+"""fp64 CPU oracle (test infrastructure only; see oracle.fp64)."""
+from .fp64 import (  # noqa: F401
+    LOG2E,
+    NEG_INF,
+    attention,
+    attention_base2,
+    attention_selected_rows,
+    block_state,
+    combine,
+    combine_partials,
+    decode_partials,
+    identity_state,
+    inject,
+    logsumexp_from_state,
+    readout,
+    safe_softmax_rows,
+    split_bounds,
+)
