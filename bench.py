@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward and split-KV decode on one MI355X.
+
+Prints ONE JSON line. A step is one fa_forward over the headline workload
+(bf16, B=2, H=32, N=8192, D=128, causal, q and k ~ N(0, 9)); `value` is its
+throughput in TFLOP/s under the 4*B*H*N^2*D (halved for causal) convention.
+The same line carries the split-KV decode (bf16, B=16, H=32, one query row, 32768
+keys, D=128, 64 chunks of 512) as HBM GB/s, the other prefill workloads' rates,
+a live roofline of the dominant kernel, a sampled parity check of the timed
+outputs against the fp64 oracle, and the oracle itself timed on the host cores.
+
+Timing: inputs are resident in HBM before the timed region; W untimed warm-up
+steps, then K steps bracketed by torch.cuda.synchronize() and HIP events recorded
+on the stream the kernels are launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+HEADLINE = "large_score_causal_d128"
+DECODE = "split_kv_decode"
+EXTRA = ["batched_prefill_d64", "batched_prefill_d64_causal", "long_context_causal_32768",
+         "long_context_causal_32767"]
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": "exact_io_aware_22_amd/csrc/fwd_bf16.hip",
+    "decode_partials_kernel": "exact_io_aware_22_amd/csrc/decode.hip",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(rel: str) -> str:
+    return hashlib.sha256((ROOT / rel).read_bytes()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they were
+    taken on the current kernel source (else None)."""
+    f = ROOT / "profiles" / "pmc_traffic.json"
+    if not f.exists():
+        return None
+    try:
+        rec = json.loads(f.read_text()).get(kernel, {}).get(workload)
+    except (ValueError, AttributeError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int, torch):
+    """Average milliseconds per call of fn(), HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def bench_prefill(name: str, steps: int, warmup: int, torch, fa, make_inputs, W, check_rows=0):
+    w = W[name]
+    q, k, v = make_inputs(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty(w.B, w.H, w.N, w.D, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+    ms = time_launches(lambda: fa.fa_forward(qd, kd, vd, o, lse, w.scale, w.causal), steps, warmup,
+                       torch)
+    res = {"workload": name, "ms": ms, "tflops": w.flops() / (ms * 1e-3) / 1e12}
+    if check_rows:
+        res["parity"] = sampled_parity(w, q, k, v, o, lse, check_rows)
+    del qd, kd, vd, o, lse
+    return res, (q, k, v)
+
+
+def sampled_parity(w, q, k, v, o, lse, n_rows):
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(12345)
+    rows = [(int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.N)))
+            for _ in range(n_rows)] + [(w.B - 1, w.H - 1, w.N - 1), (0, 0, 0)]
+    o_ref, l_ref = oracle.attention_selected_rows(q, k, v, w.scale, w.causal, rows)
+    idx = tuple(np.array(rows).T)
+    og = o.cpu().double().numpy()[idx]
+    lg = lse.cpu().double().numpy()[idx]
+    return {"rows": len(rows), "max_abs_err_o": float(np.max(np.abs(og - o_ref))),
+            "max_abs_err_lse": float(np.max(np.abs(lg - l_ref))), "tol_o": 2e-2, "tol_lse": 1e-3}
+
+
+def bench_decode(steps: int, warmup: int, torch, fa, make_inputs, W):
+    import numpy as np
+
+    import oracle
+
+    w = W[DECODE]
+    log(f"drawing {DECODE} inputs")
+    q, k, v = make_inputs(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    BH, S, D = w.B * w.H, w.splits, w.D
+    m = torch.empty(BH, S, device="cuda")
+    d = torch.empty(BH, S, device="cuda")
+    op = torch.empty(BH, S, D, device="cuda")
+    o = torch.empty(BH, D, device="cuda")
+    lse = torch.empty(BH, device="cuda")
+
+    def partials():
+        fa.fa_decode_partials(qd, kd, vd, m, d, op, w.scale, S)
+
+    def combine():
+        fa.fa_combine_partials(m, d, op, o, lse)
+
+    def step():
+        partials()
+        combine()
+
+    ms_step = time_launches(step, steps, warmup, torch)
+    ms_part = time_launches(partials, steps, warmup, torch)
+    ms_comb = time_launches(combine, steps, warmup, torch)
+    esz = 2
+    kv_bytes = 2 * w.B * w.H * w.L * w.D * esz
+    q_bytes = w.B * w.H * w.D * esz
+    out_bytes = BH * D * 4 + BH * 4
+    step_bytes = kv_bytes + q_bytes + out_bytes
+    part_bytes = kv_bytes + q_bytes
+    achieved = part_bytes / (ms_part * 1e-3) / 1e9
+    traffic = measured_traffic("decode_partials_kernel", DECODE)
+    # sampled parity: a few heads through the oracle
+    heads = [(0, 0), (15, 31), (7, 13)]
+    errs_o, errs_l = [], []
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    for b, h in heads:
+        o_ref, l_ref = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                        w.scale, False)
+        r = b * w.H + h
+        errs_o.append(float(np.max(np.abs(og[r] - o_ref[0, 0, 0]))))
+        errs_l.append(float(abs(lg[r] - l_ref[0, 0, 0])))
+    res = {
+        "workload": DECODE, "value": step_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
+        "ms_per_step": ms_step, "ms_partials": ms_part, "ms_combine": ms_comb,
+        "bytes_per_step": step_bytes,
+        "config": {"B": w.B, "H": w.H, "L": w.L, "D": w.D, "splits": S, "dtype": "bf16"},
+        "roofline": {"kernel": "decode_partials_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
+        "parity": {"heads": len(heads), "max_abs_err_o": max(errs_o), "max_abs_err_lse": max(errs_l)},
+    }
+    del qd, kd, vd
+    return res
+
+
+def cpu_baseline(q, k, v, w, budget_s: float):
+    """The fp64 oracle, as it is, on whole heads of the headline workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    heads, t_used = 0, 0.0
+    try:
+        if ctx:
+            ctx.__enter__()
+        t0 = time.perf_counter()
+        for b in range(w.B):
+            for h in range(w.H):
+                oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                 w.scale, w.causal, row_block=512, workers=cores)
+                heads += 1
+                t_used = time.perf_counter() - t0
+                if t_used >= budget_s:
+                    break
+            if t_used >= budget_s:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    flops = w.flops() / (w.B * w.H) * heads
+    cpu = "unknown"
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name} (all {w.N} rows each), fp64 numpy, "
+                      f"BLAS 1 thread per worker",
+            "seconds": t_used, "cpu_model": cpu}
+
+
+def copy_calibration(torch, nbytes: int, steps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "steps": steps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build measures one MI355X; there is no "
+              "multi-GPU path to time (--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_io_aware_22_amd import fa
+    from exact_io_aware_22_amd.workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        return 1
+    fa.load()
+    torch.cuda.set_device(0)
+
+    if args.only == "copy":
+        copy_calibration(torch, 1 << 30, args.steps)
+        return 0
+
+    out = {"metric": METRIC}
+    if args.only in ("all", "prefill"):
+        w = WORKLOADS[HEADLINE]
+        log(f"timing {HEADLINE}")
+        head, (q, k, v) = bench_prefill(HEADLINE, args.steps, args.warmup, torch, fa, make_inputs,
+                                        WORKLOADS, check_rows=64 if args.only == "all" else 0)
+        ms = head["ms"]
+        flops = w.flops()
+        achieved = flops / (ms * 1e-3) / 1e12
+        out.update({
+            "value": achieved, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": HEADLINE, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                       "causal": w.causal, "sigma_qk": w.sigma_qk, "parallelism": "single GPU"},
+            "roofline": {"kernel": "fwd_bf16_kernel", "bound": "mfma", "achieved": achieved,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_BF16_TFLOPS,
+                         "traffic": measured_traffic("fwd_bf16_kernel", HEADLINE),
+                         "algorithmic_flops_per_launch": flops},
+        })
+        if "parity" in head:
+            out["parity"] = head["parity"]
+        if args.only == "all" and not args.no_cpu_baseline:
+            log("timing the fp64 oracle on host cores")
+            out["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_seconds)
+        del q, k, v
+        if args.only == "all" and not args.no_extra:
+            out["also"] = []
+            for name in EXTRA:
+                log(f"timing {name}")
+                r, _ = bench_prefill(name, max(3, args.steps // 2), max(1, args.warmup // 2), torch,
+                                     fa, make_inputs, WORKLOADS)
+                r["frac_of_bf16_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
+                out["also"].append(r)
+                torch.cuda.empty_cache()
+    if args.only in ("all", "decode"):
+        log(f"timing {DECODE}")
+        out["decode"] = bench_decode(args.steps, args.warmup, torch, fa, make_inputs, WORKLOADS)
+        if args.only == "decode":
+            dec = out["decode"]
+            out.update({"value": dec["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                        "warmup": args.warmup, "ms_per_step": dec["ms_per_step"],
+                        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                        "dtype": "bf16", "data": "synthetic",
+                        "config": {"workload": DECODE, "parallelism": "single GPU"},
+                        "roofline": dec["roofline"]})
+    out["host"] = platform.node()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

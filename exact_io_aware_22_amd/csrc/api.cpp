@@ -1,0 +1,98 @@
+// C ABI of libfa.so (declared in include/fa.h): argument validation, then dispatch
+// to the HIP kernel launchers. Validation makes no HIP call, so every error path
+// below can be exercised on a machine without a GPU.
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Element count a*b*c*d must stay below 2^62 so every byte offset fits in int64.
+bool count_ok(int64_t a, int64_t b, int64_t c, int64_t d) {
+  const int64_t lim = int64_t(1) << 62;
+  int64_t x = a;
+  for (int64_t y : {b, c, d}) {
+    if (y != 0 && x > lim / y) return false;
+    x *= y;
+  }
+  return x < lim / 4;
+}
+
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return 1; }
+
+const char* fa_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape: negative size, D not 64 or 128, splits < 1, or too large";
+    case FA_ERR_DTYPE: return "unsupported dtype (expected FA_F32 or FA_BF16)";
+    case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, m/d/lse 4-byte alignment)";
+    case FA_ERR_ARG: return "invalid argument: scale must be finite and > 0, causal 0 or 1";
+    case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    default: return "unknown fa error code";
+  }
+}
+
+int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+               int H, int N, int D, float scale, int causal, int dtype, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || !head_dim_ok(D) || !count_ok(B, H, N, D)) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;  // empty: no pointer is touched
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, D, scale, causal == 1};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+int fa_decode_partials(const void* q, const void* k, const void* v, float* m, float* d,
+                       float* o_part, int B, int H, int L, int D, float scale, int splits,
+                       int dtype, void* stream) {
+  if (B < 0 || H < 0 || L < 0 || splits < 1 || !head_dim_ok(D) || !count_ok(B, H, L, D) ||
+      !count_ok(B, H, splits, D + 2))
+    return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_ARG;
+  if (B == 0 || H == 0) return FA_OK;  // empty: no pointer is touched
+  // L == 0 is not empty: every chunk is written as the identity, so k and v may be
+  // NULL then but q, m, d and o_part may not.
+  if (!q || !m || !d || !o_part || (L > 0 && (!k || !v))) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16) ||
+      !aligned(m, 4) || !aligned(d, 4))
+    return FA_ERR_ALIGN;
+  fa::DecodeArgs a{q, k, v, m, d, o_part, B, H, L, D, scale, splits};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_decode_partials_bf16(a, s)
+                                     : fa::launch_decode_partials_f32(a, s));
+}
+
+int fa_combine_partials(const float* m, const float* d, const float* o_part, int splits,
+                        int rows, int D, float* o, float* lse, void* stream) {
+  if (rows < 0 || splits < 1 || !head_dim_ok(D) || !count_ok(rows, splits, D, 1))
+    return FA_ERR_SHAPE;
+  if (rows == 0) return FA_OK;  // empty: no pointer is touched
+  if (!m || !d || !o_part || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(m, 4) || !aligned(d, 4) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  fa::CombineArgs a{m, d, o_part, o, lse, rows, splits, D};
+  return hip_status(fa::launch_combine_partials(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

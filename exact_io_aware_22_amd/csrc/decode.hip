@@ -1,0 +1,203 @@
+// Split-KV single-query attention ("Learning FlashAttention the Hard Way -- Part 1"):
+// decode_partials writes one (m, d, o) state per chunk of keys (split-K, section
+// "Associativity is All You Need"; the state of section "The State"); combine
+// folds them with the merge of section "The Merge, and the Twist", skipping identity
+// states (section "Why Attention's Combine Still Associates"), and reads each row
+// out once as o / d with lse = M + ln D.
+//
+// decode_partials is a pure stream over K and V (about one flop per byte), so it is
+// laid out for HBM: one workgroup per (head, chunk), four wavefronts each taking
+// 8*R keys per step with 16-byte loads that tile whole key rows (R rows per
+// wave-wide load), K and V requests issued together, dot products finished with
+// cross-lane adds inside a row, and the four wavefronts' states merged in LDS.
+#include "device.h"
+#include "launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kLoads = 8;  // 16-byte loads per lane per step, per tensor
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(64 * kWaves) void decode_partials_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    float* __restrict__ Mo, float* __restrict__ Do, float* __restrict__ Op, int L, int splits,
+    int chunk, float c, float scale) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int E = 16 / ESZ;       // elements per 16-byte load
+  constexpr int LPR = D / E;        // lanes per key row
+  constexpr int RPW = 64 / LPR;     // key rows per wave-wide load
+  constexpr int KW = kLoads * RPW;  // keys per wavefront per step
+  __shared__ float sm_m[kWaves], sm_d[kWaves];
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x % splits;
+  const int64_t bh = blockIdx.x / splits;
+  const int64_t j0l = int64_t(split) * chunk;
+  const int j0 = int(j0l < L ? j0l : L);
+  const int j1 = int(j0l + chunk < L ? j0l + chunk : L);
+  const int row = lane / LPR, col = (lane % LPR) * E;
+  const int64_t rowbytes = int64_t(D) * ESZ;
+  const uint8_t* Kh = K + bh * L * rowbytes + col * ESZ;
+  const uint8_t* Vh = V + bh * L * rowbytes + col * ESZ;
+  const u32x4_t qw = load16(Q + bh * rowbytes + col * ESZ);
+
+  float m_run = kNegInf, d_run = 0.f;
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+
+  for (int jb = j0 + wave * KW; jb < j1; jb += kWaves * KW) {
+    u32x4_t kr[kLoads], vr[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int key = jb + i * RPW + row;
+      const bool ok = key < j1;
+      kr[i] = ok ? load16(Kh + int64_t(key) * rowbytes) : u32x4_t{0, 0, 0, 0};
+      vr[i] = ok ? load16(Vh + int64_t(key) * rowbytes) : u32x4_t{0, 0, 0, 0};
+    }
+    float s[kLoads];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      float p = 0.f;
+      if constexpr (BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          p = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[i][w]), as_bf16x2(qw[w]), p, false);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) p = fmaf(__uint_as_float(kr[i][w]), __uint_as_float(qw[w]), p);
+      }
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) p += __shfl_xor(p, off);
+      s[i] = (jb + i * RPW + row < j1) ? p : kNegInf;
+      mx = fmaxf(mx, s[i]);
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float m_new = fmaxf(m_run, mx);
+    const float mref = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_hw((m_run - mref) * c);
+    const float nmc = -mref * c;
+    d_run *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const float p = exp2_hw(fmaf(s[i], c, nmc));
+      d_run += p;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (BF16) {
+          o[2 * w] = fmaf(p, bf16_lo(vr[i][w]), o[2 * w]);
+          o[2 * w + 1] = fmaf(p, bf16_hi(vr[i][w]), o[2 * w + 1]);
+        } else {
+          o[w] = fmaf(p, __uint_as_float(vr[i][w]), o[w]);
+        }
+      }
+    }
+    m_run = m_new;
+  }
+
+  // Sum the rows of this wavefront (same m everywhere in the wavefront).
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    d_run += __shfl_xor(d_run, off);
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] += __shfl_xor(o[e], off);
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sm_o[wave][col + e] = o[e];
+  }
+  if (lane == 0) {
+    sm_m[wave] = m_run;
+    sm_d[wave] = d_run;
+  }
+  __syncthreads();
+
+  // Merge the wavefronts' states; write m in natural-log units of the scaled score.
+  if (tid < D) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w]);
+    const float mref = M == kNegInf ? 0.f : M;
+    float den = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2_hw((sm_m[w] - mref) * c);
+      den = fmaf(f, sm_d[w], den);
+      acc = fmaf(f, sm_o[w][tid], acc);
+    }
+    const int64_t out = bh * splits + split;
+    Op[out * D + tid] = acc;
+    if (tid == 0) {
+      Mo[out] = M == kNegInf ? kNegInf : M * scale;
+      Do[out] = den;
+    }
+  }
+}
+
+template <bool BF16, int D>
+hipError_t launch_partials(const DecodeArgs& a, hipStream_t s) {
+  const int64_t BH = int64_t(a.B) * a.H;
+  const int64_t blocks = BH * a.splits;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int chunk = int((int64_t(a.L) + a.splits - 1) / a.splits);
+  hipLaunchKernelGGL((decode_partials_kernel<BF16, D>), dim3(unsigned(blocks)), dim3(64 * kWaves),
+                     0, s, static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                     static_cast<const uint8_t*>(a.v), a.m, a.d, a.o_part, a.L, a.splits, chunk,
+                     a.scale * kLog2e, a.scale);
+  return hipGetLastError();
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ M,
+                                                    const float* __restrict__ Dn,
+                                                    const float* __restrict__ Op,
+                                                    float* __restrict__ O,
+                                                    float* __restrict__ LSE, int splits) {
+  const int64_t r = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* mr = M + r * splits;
+  const float* dr = Dn + r * splits;
+  const float* orow = Op + r * splits * D + t;
+  float mx = kNegInf;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, mr[s]);
+  const float mref = mx == kNegInf ? 0.f : mx;
+  float den = 0.f, acc = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = mr[s];
+    if (ms == kNegInf) continue;  // the identity contributes nothing
+    const float f = exp2_hw((ms - mref) * kLog2e);
+    den = fmaf(f, dr[s], den);
+    acc = fmaf(f, orow[int64_t(s) * D], acc);
+  }
+  O[r * D + t] = den > 0.f ? acc / den : 0.f;
+  if (t == 0) LSE[r] = den > 0.f ? mx + logf(den) : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_decode_partials_bf16(const DecodeArgs& a, hipStream_t s) {
+  return a.D == 128 ? launch_partials<true, 128>(a, s) : launch_partials<true, 64>(a, s);
+}
+
+hipError_t launch_decode_partials_f32(const DecodeArgs& a, hipStream_t s) {
+  return a.D == 128 ? launch_partials<false, 128>(a, s) : launch_partials<false, 64>(a, s);
+}
+
+hipError_t launch_combine_partials(const CombineArgs& a, hipStream_t s) {
+  if (a.D == 128)
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(unsigned(a.rows)), dim3(128), 0, s, a.m, a.d,
+                       a.o_part, a.o, a.lse, a.splits);
+  else
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(unsigned(a.rows)), dim3(64), 0, s, a.m, a.d,
+                       a.o_part, a.o, a.lse, a.splits);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,48 @@
+// Internal launcher interface between the C ABI (api.cpp) and the HIP kernels.
+// Arguments reaching these functions have already been validated; each returns
+// hipSuccess or the error hipLaunchKernelGGL left behind.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int B, H, N, D;
+  float scale;
+  bool causal;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* m;
+  float* d;
+  float* o_part;
+  int B, H, L, D;
+  float scale;
+  int splits;
+};
+
+struct CombineArgs {
+  const float* m;
+  const float* d;
+  const float* o_part;
+  float* o;
+  float* lse;
+  int rows, splits, D;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_decode_partials_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_partials_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine_partials(const CombineArgs& a, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,146 @@
+"""ctypes binding of libfa.so (C ABI in include/fa.h).
+
+Argument marshalling only: torch tensors are passed as raw device pointers plus
+sizes, and the current torch stream as the HIP stream. Every step of the
+computation runs in the library's HIP kernels. If the library is missing or
+cannot be loaded this module raises; there is no other code path.
+
+Functions with the C names (fa_forward, fa_decode_partials, fa_combine_partials)
+take caller-allocated outputs, as the C calls do. forward / decode are
+conveniences that allocate the outputs with torch and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(os.environ.get("FA_LIB", Path(__file__).resolve().parent / "libfa.so"))
+_lib = None
+
+FA_F32, FA_BF16 = 0, 1
+_DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
+EXPORTED = ("fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_strerror",
+            "fa_abi_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def load():
+    """Load libfa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m exact_io_aware_22_amd.build`")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_forward.restype = i
+    lib.fa_decode_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_decode_partials.restype = i
+    lib.fa_combine_partials.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.fa_combine_partials.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().fa_strerror(int(code)).decode()
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise FaError(code, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _dense(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ------------------------------------------------------------------ C-named calls
+def fa_forward(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
+    """q, k, v: [B, H, N, D] (bf16 or fp32, same dtype); o: [B, H, N, D] fp32; lse: [B, H, N] fp32."""
+    _dense(q, k, v, o, lse)
+    B, H, N, D = q.shape
+    code = load().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
+                             float(scale), int(bool(causal)), _dtype_code(q), _stream(stream))
+    _check(code, "fa_forward")
+
+
+def fa_decode_partials(q, k, v, m, d, o_part, scale: float, splits: int, stream=None) -> None:
+    """q: [B, H, 1, D] or [B, H, D]; k, v: [B, H, L, D]; m, d: [B*H, splits]; o_part: [B*H, splits, D]."""
+    _dense(q, k, v, m, d, o_part)
+    B, H, L, D = k.shape
+    code = load().fa_decode_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(d), _ptr(o_part),
+                                     B, H, L, D, float(scale), int(splits), _dtype_code(k),
+                                     _stream(stream))
+    _check(code, "fa_decode_partials")
+
+
+def fa_combine_partials(m, d, o_part, o, lse, stream=None) -> None:
+    """m, d: [rows, splits] fp32; o_part: [rows, splits, D] fp32; o: [rows, D]; lse: [rows]."""
+    _dense(m, d, o_part, o, lse)
+    rows, splits, D = o_part.shape
+    code = load().fa_combine_partials(_ptr(m), _ptr(d), _ptr(o_part), splits, rows, D,
+                                      _ptr(o), _ptr(lse), _stream(stream))
+    _check(code, "fa_combine_partials")
+
+
+# ------------------------------------------------------------------ conveniences
+def forward(q, k, v, scale: float | None = None, causal: bool = False, stream=None):
+    """Allocate O [B, H, N, D] fp32 and lse [B, H, N] fp32 and run fa_forward."""
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty(B, H, N, D, dtype=torch.float32, device=q.device)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    fa_forward(q, k, v, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def decode(q, k, v, splits: int, scale: float | None = None, stream=None, return_partials=False):
+    """Split-KV decode: partial states per chunk, then their merge. Returns
+    (o [B, H, 1, D] fp32, lse [B, H, 1] fp32) and, if asked, the partials."""
+    B, H, L, D = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = k.device
+    m = torch.empty(B * H, splits, dtype=torch.float32, device=dev)
+    d = torch.empty(B * H, splits, dtype=torch.float32, device=dev)
+    op = torch.empty(B * H, splits, D, dtype=torch.float32, device=dev)
+    o = torch.empty(B * H, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B * H, dtype=torch.float32, device=dev)
+    fa_decode_partials(q, k, v, m, d, op, scale, splits, stream)
+    fa_combine_partials(m, d, op, o, lse, stream)
+    out = (o.view(B, H, 1, D), lse.view(B, H, 1))
+    return out + ((m, d, op),) if return_partials else out

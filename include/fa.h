@@ -1,0 +1,121 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact tiled attention forward and split-KV decode
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (definitions from "Learning FlashAttention the Hard Way --
+ * Part 1", cloudrift.ai):
+ *   S = scale * Q K^T, P = row-wise softmax(S), O = P V  (section "FlashAttention:
+ *   Not So Special"), without ever writing S or P to memory: each query row folds
+ *   its key/value tiles into the state u = (m, d, o) -- running maximum, running
+ *   denominator relative to it, unnormalised output row -- where one key enters as
+ *   (s_j, 1, v_j), two states merge by rescaling each side by e^{(its max) - (new
+ *   max)} and adding (sections "The State" and "The Merge, and the Twist"), the
+ *   identity (-inf, 0, 0) pads ragged and masked keys (sections "Associativity is
+ *   All You Need" and "Why Attention's Combine Still Associates"), and the row is
+ *   read out once as o / d.  The log-sum-exp written beside O is
+ *   lse = ln sum_j e^{s_j} = m + ln d, the absolute-coordinate denominator of
+ *   section "Why Attention's Combine Still Associates", in natural-log units.
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer allocated and owned by the caller.
+ *     The library allocates nothing, keeps no pointer after a call returns and
+ *     holds no mutable global state; calls on different streams are independent.
+ *   - Tensors are dense and row-major: q, k, v are [B][H][rows][D] with D fastest.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every
+ *     call only enqueues work on it and returns; nothing synchronises the host.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Return value: FA_OK (0) or a negative FA_ERR_* code. Arguments are fully
+ *     validated before any HIP call is made, so a rejected call enqueues nothing.
+ *     Checks run in this order: sizes (FA_ERR_SHAPE), dtype, scalar arguments;
+ *     then an empty problem (B, H or N zero; B or H zero for decode; rows zero for
+ *     combine) returns FA_OK without touching any pointer, which may then be NULL;
+ *     then NULL pointers and alignment.
+ *   - NaN or Inf in the inputs is not checked; it propagates into the outputs.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k and v. Accumulation and all outputs are float32. */
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,  /* a required pointer is NULL                                  */
+  FA_ERR_SHAPE = -2, /* negative size, D not in {64, 128}, splits < 1, or a size
+                        whose element count does not fit in 63 bits                 */
+  FA_ERR_DTYPE = -3, /* dtype is neither FA_F32 nor FA_BF16                         */
+  FA_ERR_ALIGN = -4, /* q, k, v, o or o_part is not 16-byte aligned; m, d, lse not
+                        4-byte aligned                                              */
+  FA_ERR_ARG = -5,   /* scale not finite or not > 0, or causal not 0 or 1           */
+  FA_ERR_HIP = -6    /* the HIP runtime rejected the kernel launch                   */
+};
+
+/*
+ * fa_forward -- exact attention forward with log-sum-exp.
+ *
+ *   q, k, v : [B][H][N][D] elements of `dtype` (bfloat16 or float32), read only.
+ *   o       : [B][H][N][D] float32, written: o[b][h][i] = sum_j P_ij v_j.
+ *   lse     : [B][H][N] float32, written: lse[b][h][i] = ln sum_j e^{S_ij} over the
+ *             keys row i may see (-inf and an all-zero o row if it sees none).
+ *   scale   : the softmax scale multiplying Q K^T (e.g. 1/sqrt(D)); finite, > 0.
+ *   causal  : 0 = every key visible; 1 = key j visible to query i iff j <= i.
+ *   D       : head dimension, 64 or 128.
+ * Scores are formed from the inputs exactly as given, accumulated in float32; the
+ * probabilities fed to the P V product are rounded to the input type.
+ */
+int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse,
+               int B, int H, int N, int D, float scale, int causal, int dtype,
+               void* stream);
+
+/*
+ * fa_decode_partials -- split-KV single-query attention, first step.
+ * Split-K as in section "Associativity is All You Need": the L keys of every head
+ * are cut into `splits` chunks of c = ceil(L / splits) keys (chunk s covers keys
+ * [s*c, min(L, (s+1)*c)); chunks past the end are empty), and each chunk's state
+ * is written to caller-owned scratch for fa_combine_partials to fold.
+ *
+ *   q       : [B][H][D] (one query row per head) of `dtype`.
+ *   k, v    : [B][H][L][D] of `dtype`.
+ *   m, d    : [B*H][splits] float32, written. m = max_j s_j over the chunk in
+ *             natural-log units of the scaled score s_j = scale * q.k_j;
+ *             d = sum_j e^{s_j - m}, so 1 <= d <= chunk length.
+ *   o_part  : [B*H][splits][D] float32, written: sum_j e^{s_j - m} v_j (NOT
+ *             divided by d).
+ *   An empty chunk is written as the identity: m = -inf, d = 0, o_part = 0.
+ *   L may be 0 (every chunk is empty); k and v may then be NULL.
+ * Scratch size: B*H*splits*(D + 2) floats, owned and freed by the caller.
+ */
+int fa_decode_partials(const void* q, const void* k, const void* v, float* m, float* d,
+                       float* o_part, int B, int H, int L, int D, float scale, int splits,
+                       int dtype, void* stream);
+
+/*
+ * fa_combine_partials -- fold partial states with the combine of section "The
+ * Merge, and the Twist" (identity states are skipped) and read each row out once.
+ *
+ *   m, d    : [rows][splits] float32 partial maxima (natural-log units) and
+ *             denominators relative to them.
+ *   o_part  : [rows][splits][D] float32 unnormalised partial outputs.
+ *   o       : [rows][D] float32, written: the merged o / d.
+ *   lse     : [rows] float32, written: M + ln(sum_s d_s e^{m_s - M}), M = max_s m_s.
+ *   A row whose partials are all the identity is written as o = 0, lse = -inf.
+ *   rows >= 0 (0 is an empty call), splits >= 1, D in {64, 128}.
+ */
+int fa_combine_partials(const float* m, const float* d, const float* o_part, int splits,
+                        int rows, int D, float* o, float* lse, void* stream);
+
+/* Static, human-readable name of an FA_* code (never NULL). */
+const char* fa_strerror(int code);
+
+/* ABI version of this header: 1. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,124 @@
+"""Host-side checks of libfa.so: it loads, exports every call include/fa.h declares,
+and rejects bad arguments with the documented codes before touching the GPU.
+
+Nothing here launches a kernel: every call either fails validation or describes an
+empty problem, both of which return before any HIP call.
+"""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+from exact_io_aware_22_amd import fa
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "fa.h"
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ARG = 0, -1, -2, -3, -4, -5
+P = 1 << 20  # a fake, 16-byte-aligned, never dereferenced address
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not fa._LIB_PATH.exists():
+        pytest.fail("libfa.so is not built (python -m exact_io_aware_22_amd.build)")
+    return fa.load()
+
+
+def test_header_declares_the_documented_calls():
+    assert declared_functions() == sorted(
+        ["fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_strerror", "fa_abi_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(fa._LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\S+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(fa.EXPORTED) == set(declared_functions())
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.fa_abi_version() == 1
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, ARG, -6, 12345):
+        msg = fa.strerror(code)
+        assert isinstance(msg, str) and msg
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=8, D=64, scale=0.125, causal=0, dtype=1):
+    return lib.fa_forward(q, k, v, o, lse, B, H, N, D, scale, causal, dtype, None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, q=None) == NULL
+    assert fwd(lib, lse=None) == NULL
+    assert fwd(lib, N=-1) == SHAPE
+    assert fwd(lib, B=-3) == SHAPE
+    assert fwd(lib, D=96) == SHAPE
+    assert fwd(lib, D=256) == SHAPE
+    assert fwd(lib, B=1 << 30, H=1 << 30, N=1 << 30) == SHAPE
+    assert fwd(lib, dtype=7) == DTYPE
+    assert fwd(lib, q=P + 8) == ALIGN
+    assert fwd(lib, o=P + 4) == ALIGN
+    assert fwd(lib, lse=P + 2) == ALIGN
+    assert fwd(lib, scale=0.0) == ARG
+    assert fwd(lib, scale=-1.0) == ARG
+    assert fwd(lib, scale=float("nan")) == ARG
+    assert fwd(lib, scale=float("inf")) == ARG
+    assert fwd(lib, causal=2) == ARG
+    # empty problems are valid and launch nothing
+    assert fwd(lib, B=0) == OK
+    assert fwd(lib, N=0) == OK
+    assert fwd(lib, H=0, D=128, dtype=0) == OK
+    assert fwd(lib, q=None, k=None, v=None, o=None, lse=None, N=0) == OK  # empty tensors
+    assert fwd(lib, N=0, D=80) == SHAPE  # sizes are still checked first
+
+
+def dec(lib, q=P, k=P, v=P, m=P, d=P, op=P, B=1, H=1, L=64, D=128, scale=0.1, splits=4, dtype=1):
+    return lib.fa_decode_partials(q, k, v, m, d, op, B, H, L, D, scale, splits, dtype, None)
+
+
+def test_decode_validation(lib):
+    assert dec(lib, m=None) == NULL
+    assert dec(lib, splits=0) == SHAPE
+    assert dec(lib, L=-1) == SHAPE
+    assert dec(lib, D=32) == SHAPE
+    assert dec(lib, dtype=-1) == DTYPE
+    assert dec(lib, k=P + 4) == ALIGN
+    assert dec(lib, op=P + 8) == ALIGN
+    assert dec(lib, m=P + 1) == ALIGN
+    assert dec(lib, scale=0.0) == ARG
+    assert dec(lib, B=0) == OK
+    assert dec(lib, H=0) == OK
+    assert dec(lib, q=None, B=0) == OK
+    assert dec(lib, q=None, L=0) == NULL  # L = 0 is not empty: it writes identities
+
+
+def comb(lib, m=P, d=P, op=P, splits=4, rows=3, D=64, o=P, lse=P):
+    return lib.fa_combine_partials(m, d, op, splits, rows, D, o, lse, None)
+
+
+def test_combine_validation(lib):
+    assert comb(lib, o=None) == NULL
+    assert comb(lib, splits=0) == SHAPE
+    assert comb(lib, rows=-1) == SHAPE
+    assert comb(lib, D=100) == SHAPE
+    assert comb(lib, op=P + 4) == ALIGN
+    assert comb(lib, lse=P + 1) == ALIGN
+    assert comb(lib, rows=0) == OK
+    assert comb(lib, rows=0, m=None, o=None) == OK
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(fa.FaError, match="scale"):
+        fa._check(lib.fa_forward(P, P, P, P, P, 1, 1, 8, 64, -1.0, 0, 1, None), "fa_forward")
