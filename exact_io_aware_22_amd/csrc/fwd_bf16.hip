@@ -1,40 +1,56 @@
 // Exact attention forward, bfloat16 inputs, float32 accumulation, on gfx950 MFMA.
 //
 // Method ("Learning FlashAttention the Hard Way -- Part 1"): every query row folds
-// its key/value tiles into u = (m, d, o) (section "The State"); a new tile is merged
-// by rescaling the running state by 2^{(m_old - m_new) c} (section "The Merge, and
-// the Twist") with all exponentials in base 2 and log2(e) folded into the scale,
+// its keys, 32 at a time, into u = (m, d, o) (section "The State"); merging a block
+// rescales the running state by 2^{(m_old - m_new) c} (section "The Merge, and the
+// Twist") with all exponentials in base 2 and log2(e) folded into the scale,
 // c = scale * log2(e) (section "Alternative Twist: Base 2"); masked and ragged keys
 // get score -inf, i.e. they enter as the identity (section "Why Attention's Combine
 // Still Associates"); o / d is formed once at the end.
 //
-// Work decomposition (one workgroup = 4 wavefronts = 128 query rows of one head):
-//   * The scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+// Reference maximum. Any reference value r may stand in for the running maximum m:
+// (m, d, o) and (r, d e^{m-r}, o e^{m-r}) are the same state in other coordinates
+// (section "Twisted Monoid": the combine is transported by any bijection). The kernel
+// keeps r fixed until a new block's maximum exceeds it by more than 2^kTau in
+// weight, so weights stay in [0, 2^kTau] (no overflow, same relative precision) and
+// the accumulator is rescaled only on those rare steps instead of every block.
+//
+// Work decomposition (one workgroup = 8 wavefronts = 256 query rows of one head):
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     the 32x32 accumulator gives each lane one query column and 16 key rows, so a
-//     query's running max needs one cross-half exchange (v_permlane32_swap) per tile
-//     and its denominator none until the end.
+//     query's block maximum needs one cross-half exchange (v_permlane32_swap) and
+//     its denominator none until the end.
 //   * The output is accumulated transposed too, O^T += V^T P^T. The probabilities a
 //     lane holds for its query are, after bf16 packing, exactly the B operand of the
 //     PV MFMA, provided keys are assigned to the rows of the K operand in the order
 //     given by swap23() below. P never leaves registers.
-//   * Q fragments live in VGPRs for the whole loop; K and V tiles of 64 keys are
-//     staged global -> registers -> LDS, double-buffered so the next tile's global
-//     loads are in flight while the current tile is computed. K is kept row-major
-//     in LDS, V transposed (V^T), both with a 16-byte-chunk XOR swizzle so that the
-//     fragment reads are free of bank conflicts.
-//   * Causal: tiles above a wavefront's diagonal are skipped, only tiles that cross
-//     the diagonal or the ragged end of the sequence are masked, the heaviest query
-//     tiles are launched first and all tiles of one head are mapped to one XCD so
-//     its K/V stream is shared in that XCD's L2.
+//   * Each 32-key step g issues, in one basic block, the QK MFMAs of block g+1, the
+//     PV MFMAs of block g-1 and the softmax of block g, which are independent, so the
+//     compiler can interleave vector-ALU work with the matrix pipe.
+//   * K and V arrive 64 keys per tile through three-slot LDS rings (K two tiles
+//     ahead, V one tile ahead), copied global -> registers -> LDS by all threads
+//     (loads issued at the start of a tile, stores at its end), one barrier per
+//     tile. Both stay row-major in LDS with a 16-byte
+//     chunk XOR swizzle. The V^T operand of the PV MFMA is read with the transposing
+//     LDS read ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+//     element (i mod 4) of what lane 4e + i/4 addressed, for e = 0..3, so lanes that
+//     address four consecutive head dims of four consecutive keys hand each lane
+//     four keys of one head dim.
+//   * Causal: a wavefront stops at its diagonal block, which is the only block it
+//     masks (plus the ragged tail); heaviest query tiles launch first and all tiles
+//     of a head go to one XCD so its K/V stream is shared in that XCD's L2.
 #include "device.h"
 #include "launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kBM = 128;  // query rows per workgroup (32 per wavefront)
-constexpr int kBN = 64;   // keys per LDS tile
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per LDS tile (two 32-key blocks)
+constexpr int kSlots = 3;         // LDS ring depth for K and for V
+constexpr float kTau = 8.0f;      // rescale when the maximum grows by more than 2^8
 
 // Row r of a 32-row K operand block holds key swap23(r): bits 2 and 3 exchanged.
 // With this order the accumulator registers 8c..8c+7 of a lane hold 8 consecutive
@@ -48,17 +64,32 @@ __device__ __forceinline__ int swap23(int r) {
 // to 8 distinct chunk slots.
 __device__ __forceinline__ int kswz(int key) { return (key & 3) | ((key >> 1) & 4); }
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+#define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
 template <int D>
-struct Tile {
-  static constexpr int NCH = D / 16;          // 16-wide k chunks of the head dim
-  static constexpr int NDB = D / 32;          // 32-row blocks of O^T
-  static constexpr int KROW = D * 2;          // bytes per K row in LDS
-  static constexpr int VTROW = kBN * 2;       // bytes per V^T row in LDS
-  static constexpr int KBYTES = kBN * KROW;
-  static constexpr int STAGE = KBYTES + D * VTROW;
-  static constexpr int KLOADS = kBN * D / 8 / kThreads;  // 16-byte K loads per thread
-  static constexpr int VGROUPS = (D / 8) * (kBN / 4);    // 4-key x 8-dim V blocks
+struct Geo {
+  static constexpr int NCH = D / 16;           // 16-wide k chunks of the head dim
+  static constexpr int NDB = D / 32;           // 32-row blocks of O^T
+  static constexpr int KROW = D * 2;           // bytes per K row in LDS
+  static constexpr int KTILE = kBN * KROW;     // bytes of one K tile
+  static constexpr int LDS = kSlots * 2 * KTILE;  // K ring then V ring
+  static constexpr int CPR = KROW / 16;              // 16-byte chunks per row
+  static constexpr int SPT = KTILE / 16 / kThreads;  // chunks of a tile per thread
 };
+
+// XOR on the 16-byte chunk index of V row `key`: the transposing reads of one
+// 16-lane group touch 4 consecutive keys x 32 bytes, which this spreads over
+// distinct banks (with 32 or 64 LDS banks alike).
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+  if constexpr (D == 128) {
+    constexpr uint32_t kX = 0x0ca60u;  // 0, 6, 10, 12 as 4-bit fields
+    return (kX >> (4 * (key & 3))) & 15;
+  } else {
+    return 2 * (key & 3);
+  }
+}
 
 // Workgroup -> (head, query tile). Workgroups are dispatched round-robin over the
 // 8 XCDs; all query tiles of a head go to the same XCD, heaviest (causal) first.
@@ -76,12 +107,14 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nqt, bool causal, 
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
     int BH, int nqt, float c) {
-  using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
+  uint8_t* const kring = smem;
+  uint8_t* const vring = smem + kSlots * G::KTILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -93,177 +126,205 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
 
-  // Q^T fragments (B operand): lane holds Q[qrow][16c + 8*half .. +7].
-  const int qrow = q0 + wave * 32 + l32;
-  u32x4_t qf[T::NCH];
+  // Blocks of 32 keys: this wavefront folds blocks [0, nblk); the workgroup stages
+  // tiles [0, ntiles) covering the most any of its wavefronts needs.
+  const int qw0 = q0 + 32 * wave;  // first query row of this wavefront
+  const int nblk_all = (N + 31) >> 5;
+  const int nblk = qw0 >= N ? 0 : (CAUSAL ? min(nblk_all, (qw0 >> 5) + 1) : nblk_all);
+  const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kBM) - 1) >> 5) + 1) : nblk_all;
+  const int ntiles = (nblk_wg + 1) >> 1;
+
+  // ---- staging: each thread copies SPT 16-byte chunks of a K tile and SPT of a V
+  // tile, global -> registers at the start of a tile, registers -> LDS at its end.
+  // Thread chunk idx fills physical slot idx % CPR of row idx / CPR and fetches the
+  // logical chunk the row's swizzle puts there. Rows past the end of the sequence
+  // are zero, so masked keys meet finite values (zero weight times zero).
+  u32x4_t stg[2 * G::SPT];
+  auto gload = [&](int tk, int tv) {
 #pragma unroll
-  for (int c2 = 0; c2 < T::NCH; ++c2)
+    for (int i = 0; i < 2 * G::SPT; ++i) {
+      const bool is_v = i >= G::SPT;
+      const int idx = tid + kThreads * (i % G::SPT);
+      const int row = idx / G::CPR, pslot = idx % G::CPR;
+      const int lchunk = pslot ^ (is_v ? vswz<D>(row) : kswz(row));
+      const int t = max(is_v ? tv : tk, 0);
+      const int gk = min(t * kBN + row, N - 1);  // always a real row; zeroed at the store
+      stg[i] = load16((is_v ? Vh : Kh) + int64_t(gk) * D + lchunk * 8);
+    }
+  };
+  auto lstore = [&](int tk, int tv) {
+#pragma unroll
+    for (int i = 0; i < 2 * G::SPT; ++i) {
+      const bool is_v = i >= G::SPT;
+      const int t = is_v ? tv : tk;
+      if (t < 0) continue;
+      uint8_t* tile = (is_v ? vring : kring) + (t % kSlots) * G::KTILE;
+      const int idx = tid + kThreads * (i % G::SPT);
+      const bool real = t * kBN + idx / G::CPR < N;
+      *reinterpret_cast<u32x4_t*>(tile + idx * 16) = real ? stg[i] : u32x4_t{0, 0, 0, 0};
+    }
+  };
+
+  // ---- per-lane state: Q^T fragments, O^T accumulator, reference max r, d
+  const int qrow = qw0 + l32;
+  u32x4_t qf[G::NCH];
+#pragma unroll
+  for (int c2 = 0; c2 < G::NCH; ++c2)
     qf[c2] = qrow < N ? load16(Qh + int64_t(qrow) * D + 16 * c2 + 8 * half) : u32x4_t{0, 0, 0, 0};
-
-  const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
-
-  // ---- staging of one K/V tile: global -> registers -> LDS
-  u32x4_t kst[T::KLOADS];
-  u32x4_t vst[4];
-  const bool v_loader = T::VGROUPS >= kThreads || tid < T::VGROUPS;
-  const int vdg = tid % (D / 8), vkg = tid / (D / 8);
-
-  auto gload = [&](int t) {
-    const int k0 = t * kBN;
+  f32x16_t oacc[G::NDB];
 #pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int key = idx / (D / 8), cc = idx % (D / 8);
-      const int gk = k0 + key;
-      kst[i] = gk < N ? load16(Kh + int64_t(gk) * D + cc * 8) : u32x4_t{0, 0, 0, 0};
+  for (int db = 0; db < G::NDB; ++db) oacc[db] = f32x16_t{};
+  // d_lse sums the weights in float32 (for the log-sum-exp); d_out sums the same
+  // weights as rounded to bf16 for the PV MFMA, so O is normalised by exactly the
+  // weights it was built from.
+  float m_ref = kNegInf, d_lse = 0.f, d_out = 0.f;
+
+  // S^T block g (32 keys x this wavefront's 32 queries) from the K ring.
+  auto qk = [&](int g) {
+    const uint8_t* ks = kring + ((g >> 1) % kSlots) * G::KTILE;
+    const int key = (g & 1) * 32 + swap23(l32);
+    const uint8_t* krow = ks + key * G::KROW;
+    const int sw = kswz(key);
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int c2 = 0; c2 < G::NCH; ++c2) {
+      const u32x4_t a = load16(krow + (((2 * c2 + half) ^ sw) << 4));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[c2]), s, 0, 0, 0);
     }
-    if (v_loader) {
+    return s;
+  };
+  // O^T += V^T (block g) P^T (block g). The A operand (rows = head dims 32db + l32,
+  // k = keys 16cc + 8*half + 0..7 of the block) comes from two transposing reads:
+  // lane j of each 16-lane group addresses key 4*r + j/4 (r = 0, 1) and head dims
+  // 4*(j%4) .. +3 of the group's 16 dims.
+  const int tr_key = (lane & 15) >> 2;
+  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto pv = [&](int g, const uint32_t (&pk)[8]) {
+    const uint8_t* vs = vring + ((g >> 1) % kSlots) * G::KTILE;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gk = k0 + 4 * vkg + r;
-        vst[r] = gk < N ? load16(Vh + int64_t(gk) * D + vdg * 8) : u32x4_t{0, 0, 0, 0};
+    for (int cc = 0; cc < 2; ++cc) {
+      const u32x4_t b = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        const int dim = 32 * db + tr_dim;
+        v4i16_t lo, hi;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int key = 32 * (g & 1) + 16 * cc + 8 * half + 4 * r + tr_key;
+          const int chunk = (dim >> 3) ^ vswz<D>(key);
+          const uint8_t* a = vs + key * G::KROW + (chunk << 4) + ((dim & 4) << 1);
+          const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a));
+          if (r == 0) lo = x; else hi = x;
+        }
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t a = {l2[0], l2[1], h2[0], h2[1]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b),
+                                                           oacc[db], 0, 0, 0);
       }
     }
   };
-  auto lstore = [&](int buf) {
-    uint8_t* ks = smem + buf * T::STAGE;
-    uint8_t* vs = ks + T::KBYTES;
+  // Softmax of block g against the reference maximum; returns the factor the
+  // accumulator must be multiplied by once block g-1 has been added (1 if unchanged).
+  auto apply_mask = [&](int g, f32x16_t& s) {
+    const int qi = qw0 + l32;
 #pragma unroll
-    for (int i = 0; i < T::KLOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int key = idx / (D / 8), cc = idx % (D / 8);
-      *reinterpret_cast<u32x4_t*>(ks + key * T::KROW + ((cc ^ kswz(key)) << 4)) = kst[i];
-    }
-    if (v_loader) {
-      // Transpose a 4-key x 8-dim block: row d of V^T receives keys 4*vkg .. +3.
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = vdg * 8 + e;
-        const uint32_t a0 = vst[0][e >> 1], a1 = vst[1][e >> 1];
-        const uint32_t a2 = vst[2][e >> 1], a3 = vst[3][e >> 1];
-        const uint32_t w0 = (e & 1) ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        const uint32_t w1 = (e & 1) ? ((a2 >> 16) | (a3 & 0xffff0000u)) : ((a2 & 0xffffu) | (a3 << 16));
-        const int off = d * T::VTROW + ((((vkg >> 1) ^ (d & 7))) << 4) + ((vkg & 1) << 3);
-        *reinterpret_cast<u32x2_t*>(vs + off) = u32x2_t{w0, w1};
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * g + swap23(8 * (r >> 2) + 4 * half + (r & 3));
+      if (key >= N || (CAUSAL && key > qi)) s[r] = kNegInf;
     }
   };
-
-  // ---- running state of this lane's query: m (raw score units), d (this half's keys)
-  f32x16_t oacc[T::NDB];
+  auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8]) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-  for (int db = 0; db < T::NDB; ++db) oacc[db] = f32x16_t{};
-  float m_run = kNegInf, d_run = 0.f;
+    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+    mx = fmaxf(mx, s[15]);
+    mx = halves_max(mx);
+    const bool grow = (mx - m_ref) * c > kTau;  // false when both are -inf
+    const float m_new = grow ? mx : m_ref;
+    const float alpha = grow ? exp2_hw((m_ref - m_new) * c) : 1.f;
+    const float nmc = m_new == kNegInf ? 0.f : -m_new * c;
+    float ps = 0.f, pq = 0.f;
+    const bf16x2_t ones = as_bf16x2(0x3f803f80u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = exp2_hw(fmaf(s[2 * i], c, nmc));
+      const float p1 = exp2_hw(fmaf(s[2 * i + 1], c, nmc));
+      ps += p0 + p1;
+      pk[i] = pack_bf16x2(p0, p1);
+      pq = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[i]), ones, pq, false);
+    }
+    d_lse = fmaf(d_lse, alpha, ps);
+    d_out = fmaf(d_out, alpha, pq);
+    m_ref = m_new;
+    return alpha;
+  };
+  auto rescale = [&](float alpha) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) oacc[db] *= alpha;
+    }
+  };
+  auto needs_mask = [&](int g) { return (32 * g + 32 > N) || (CAUSAL && 32 * g + 31 > qw0); };
 
-  gload(0);
-  lstore(0);
+  // ---- prologue: K tiles 0 and 1, V tile 0
+  gload(0, 0);
+  lstore(0, 0);
+  if (ntiles > 1) {
+    gload(1, -1);
+    lstore(1, -1);
+  }
   __syncthreads();
 
-  const int qw_first = q0 + wave * 32;  // first query row of this wavefront
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gload(t + 1);
-    const int k0 = t * kBN;
-    const bool active = !CAUSAL || k0 <= qw_first + 31;
-    if (active) {
-      const uint8_t* ks = smem + (t & 1) * T::STAGE;
-      const uint8_t* vs = ks + T::KBYTES;
+  f32x16_t s_cur = f32x16_t{};
+  uint32_t p_prev[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (nblk > 0) s_cur = qk(0);
 
-      // S^T block kb: rows = keys k0 + 32kb + swap23(row), columns = this wave's queries.
-      f32x16_t s[2];
+  // One iteration per 32-key block; tiles (two blocks) are staged on even blocks
+  // and published after odd ones. Slots (t+2)%3 of K and (t+1)%3 of V, refilled at
+  // the start of tile t, were last read during tile t-1.
+  // A step is one basic block: QK of block g+1 (issued even past a wavefront's last
+  // block, reading a resident slot, result unused), PV of block g-1 (at g = 0 with
+  // zero weights against tile 0) and the softmax of block g. The only branches are
+  // the mask of the diagonal / ragged block, applied first, and the rare rescale.
+#pragma unroll 1
+  for (int g = 0; g < 2 * ntiles; ++g) {
+    const int t = g >> 1;
+    const int tk = t + 2 < ntiles ? t + 2 : -1, tv = t + 1 < ntiles ? t + 1 : -1;
+    if ((g & 1) == 0 && (tk >= 0 || tv >= 0)) gload(tk, tv);
+    if (g < nblk) {
+      if (needs_mask(g)) apply_mask(g, s_cur);
+      uint32_t p_cur[8];
+      const f32x16_t s_next = qk(g + 1);
+      pv(g > 0 ? g - 1 : 0, p_prev);
+      const float alpha = softmax(s_cur, p_cur);
+      s_cur = s_next;
+      rescale(alpha);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
-        const int key = kb * 32 + swap23(l32);
-        const uint8_t* krow = ks + key * T::KROW;
-        const int sw = kswz(key);
-#pragma unroll
-        for (int c2 = 0; c2 < T::NCH; ++c2) {
-          const u32x4_t a = load16(krow + (((2 * c2 + half) ^ sw) << 4));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[c2]),
-                                                          s[kb], 0, 0, 0);
-        }
-      }
-
-      // Neutral-element masking, only on tiles that reach past the end or the diagonal.
-      const bool need_mask = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > qw_first);
-      if (need_mask) {
-        const int qi = qw_first + l32;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + swap23(8 * (r >> 2) + 4 * half + (r & 3));
-            if (key >= N || (CAUSAL && key > qi)) s[kb][r] = kNegInf;
-          }
-      }
-
-      // Tile maximum of this query (16 keys per lane per block, then the other half).
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      // Reference point for the exponentials; a still-empty state stays the identity.
-      const float mref = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_hw((m_run - mref) * c);
-      const float nmc = -mref * c;
-
-      uint32_t pk[2][8];
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p0 = exp2_hw(fmaf(s[kb][2 * i], c, nmc));
-          const float p1 = exp2_hw(fmaf(s[kb][2 * i + 1], c, nmc));
-          ps += p0 + p1;
-          pk[kb][i] = pack_bf16x2(p0, p1);
-        }
-      d_run = d_run * alpha + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < T::NDB; ++db) oacc[db] *= alpha;
-
-      // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const u32x4_t b = {pk[kb][4 * cc], pk[kb][4 * cc + 1], pk[kb][4 * cc + 2],
-                             pk[kb][4 * cc + 3]};
-          const int ch = 4 * kb + 2 * cc + half;  // 16-byte chunk of keys in a V^T row
-#pragma unroll
-          for (int db = 0; db < T::NDB; ++db) {
-            const int d = 32 * db + l32;
-            const u32x4_t a = load16(vs + d * T::VTROW + ((ch ^ (d & 7)) << 4));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b),
-                                                               oacc[db], 0, 0, 0);
-          }
-        }
+      for (int i = 0; i < 8; ++i) p_prev[i] = p_cur[i];
+      if (g + 1 == nblk) pv(g, p_prev);  // last block: fold it in while V is resident
     }
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
-    __syncthreads();
+    if (g & 1) {
+      if (tk >= 0 || tv >= 0) lstore(tk, tv);
+      __syncthreads();
+    }
   }
 
-  // ---- read out: o / d once, lse = ln(sum) = (m c + log2 d) ln 2
-  const float dt = halves_sum(d_run);
-  const int qi = qw_first + l32;
+  // ---- read out: o / d once, lse = ln(sum) = (r c + log2 d) ln 2
+  const float dl = halves_sum(d_lse), dq = halves_sum(d_out);
+  const int qi = qw0 + l32;
   if (qi < N) {
-    const float inv = dt > 0.f ? 1.f / dt : 0.f;
+    const float inv = dq > 0.f ? 1.f / dq : 0.f;
     float* orow = O + head + int64_t(qi) * D;
 #pragma unroll
-    for (int db = 0; db < T::NDB; ++db)
+    for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4_t val = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                             oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
-        *reinterpret_cast<f32x4_t*>(orow + 32 * db + 8 * g + 4 * half) = val;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4_t val = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
+                             oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+        *reinterpret_cast<f32x4_t*>(orow + 32 * db + 8 * g4 + 4 * half) = val;
       }
     if (half == 0)
-      LSE[int64_t(bh) * N + qi] = dt > 0.f ? (m_run * c + log2_hw(dt)) * kLn2 : kNegInf;
+      LSE[int64_t(bh) * N + qi] = dl > 0.f ? (m_ref * c + log2_hw(dl)) * kLn2 : kNegInf;
   }
 }
 
