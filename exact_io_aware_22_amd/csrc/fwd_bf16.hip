@@ -13,7 +13,10 @@
 // (section "Twisted Monoid": the combine is transported by any bijection). The kernel
 // keeps r fixed until a new block's maximum exceeds it by more than 2^kTau in
 // weight, so weights stay in [0, 2^kTau] (no overflow, same relative precision) and
-// the accumulator is rescaled only on those rare steps instead of every block.
+// the accumulator is rescaled only on those rare steps instead of every block. O is
+// normalised by the sum of the weights as rounded to bf16 for the PV product, so it
+// is divided by exactly the weights it was built from; the log-sum-exp uses the
+// float32 sum.
 //
 // Work decomposition (one workgroup = 8 wavefronts = 256 query rows of one head):
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -26,16 +29,18 @@
 //     given by swap23() below. P never leaves registers.
 //   * Each 32-key step g issues, in one basic block, the QK MFMAs of block g+1, the
 //     PV MFMAs of block g-1 and the softmax of block g, which are independent, so the
-//     compiler can interleave vector-ALU work with the matrix pipe.
+//     hardware overlaps vector-ALU work with the matrix pipe.
 //   * K and V arrive 64 keys per tile through three-slot LDS rings (K two tiles
 //     ahead, V one tile ahead), copied global -> registers -> LDS by all threads
 //     (loads issued at the start of a tile, stores at its end), one barrier per
-//     tile. Both stay row-major in LDS with a 16-byte
-//     chunk XOR swizzle. The V^T operand of the PV MFMA is read with the transposing
-//     LDS read ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
-//     element (i mod 4) of what lane 4e + i/4 addressed, for e = 0..3, so lanes that
-//     address four consecutive head dims of four consecutive keys hand each lane
-//     four keys of one head dim.
+//     tile. Both are row-major in LDS with padded rows (K: +16 bytes, V: +64 bytes),
+//     which keeps the fragment reads free of bank conflicts on 64 LDS banks and
+//     makes every fragment address one per-lane base plus a constant.
+//   * The V^T operand of the PV MFMA is read with the transposing LDS read
+//     ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+//     (i mod 4) of what lane 4e + i/4 addressed, for e = 0..3, so lanes that address
+//     four consecutive head dims of four consecutive keys hand each lane four keys
+//     of one head dim.
 //   * Causal: a wavefront stops at its diagonal block, which is the only block it
 //     masks (plus the ragged tail); heaviest query tiles launch first and all tiles
 //     of a head go to one XCD so its K/V stream is shared in that XCD's L2.
@@ -59,37 +64,21 @@ __device__ __forceinline__ int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// XOR applied to the 16-byte chunk index of K row `key` in LDS. The 8 lanes that
-// read together touch keys {0,1,2,3,8,9,10,11} + const (or +4), which this maps
-// to 8 distinct chunk slots.
-__device__ __forceinline__ int kswz(int key) { return (key & 3) | ((key >> 1) & 4); }
-
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 #define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <int D>
 struct Geo {
-  static constexpr int NCH = D / 16;           // 16-wide k chunks of the head dim
-  static constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  static constexpr int KROW = D * 2;           // bytes per K row in LDS
-  static constexpr int KTILE = kBN * KROW;     // bytes of one K tile
-  static constexpr int LDS = kSlots * 2 * KTILE;  // K ring then V ring
-  static constexpr int CPR = KROW / 16;              // 16-byte chunks per row
-  static constexpr int SPT = KTILE / 16 / kThreads;  // chunks of a tile per thread
+  static constexpr int NCH = D / 16;             // 16-wide k chunks of the head dim
+  static constexpr int NDB = D / 32;             // 32-row blocks of O^T
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int KSTRIDE = D * 2 + 16;     // bytes per K row in LDS
+  static constexpr int VSTRIDE = D * 2 + 64;     // bytes per V row in LDS
+  static constexpr int KTILE = kBN * KSTRIDE;
+  static constexpr int VTILE = kBN * VSTRIDE;
+  static constexpr int LDS = kSlots * (KTILE + VTILE);
+  static constexpr int SPT = kBN * CPR / kThreads;  // chunks of a tile per thread
 };
-
-// XOR on the 16-byte chunk index of V row `key`: the transposing reads of one
-// 16-lane group touch 4 consecutive keys x 32 bytes, which this spreads over
-// distinct banks (with 32 or 64 LDS banks alike).
-template <int D>
-__device__ __forceinline__ int vswz(int key) {
-  if constexpr (D == 128) {
-    constexpr uint32_t kX = 0x0ca60u;  // 0, 6, 10, 12 as 4-bit fields
-    return (kX >> (4 * (key & 3))) & 15;
-  } else {
-    return 2 * (key & 3);
-  }
-}
 
 // Workgroup -> (head, query tile). Workgroups are dispatched round-robin over the
 // 8 XCDs; all query tiles of a head go to the same XCD, heaviest (causal) first.
@@ -116,7 +105,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   uint8_t* const kring = smem;
   uint8_t* const vring = smem + kSlots * G::KTILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int half = lane >> 5, l32 = lane & 31;
   int bh, qt;
   map_tile(blockIdx.x, BH, nqt, CAUSAL, bh, qt);
@@ -136,20 +126,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   // ---- staging: each thread copies SPT 16-byte chunks of a K tile and SPT of a V
   // tile, global -> registers at the start of a tile, registers -> LDS at its end.
-  // Thread chunk idx fills physical slot idx % CPR of row idx / CPR and fetches the
-  // logical chunk the row's swizzle puts there. Rows past the end of the sequence
-  // are zero, so masked keys meet finite values (zero weight times zero).
+  // Rows past the end of the sequence are stored as zeros, so masked keys meet
+  // finite values (zero weight times zero); the load itself reads the last row.
   u32x4_t stg[2 * G::SPT];
   auto gload = [&](int tk, int tv) {
 #pragma unroll
     for (int i = 0; i < 2 * G::SPT; ++i) {
       const bool is_v = i >= G::SPT;
       const int idx = tid + kThreads * (i % G::SPT);
-      const int row = idx / G::CPR, pslot = idx % G::CPR;
-      const int lchunk = pslot ^ (is_v ? vswz<D>(row) : kswz(row));
       const int t = max(is_v ? tv : tk, 0);
-      const int gk = min(t * kBN + row, N - 1);  // always a real row; zeroed at the store
-      stg[i] = load16((is_v ? Vh : Kh) + int64_t(gk) * D + lchunk * 8);
+      const int gk = min(t * kBN + idx / G::CPR, N - 1);
+      stg[i] = load16((is_v ? Vh : Kh) + int64_t(gk) * D + (idx % G::CPR) * 8);
     }
   };
   auto lstore = [&](int tk, int tv) {
@@ -158,10 +145,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       const bool is_v = i >= G::SPT;
       const int t = is_v ? tv : tk;
       if (t < 0) continue;
-      uint8_t* tile = (is_v ? vring : kring) + (t % kSlots) * G::KTILE;
       const int idx = tid + kThreads * (i % G::SPT);
-      const bool real = t * kBN + idx / G::CPR < N;
-      *reinterpret_cast<u32x4_t*>(tile + idx * 16) = real ? stg[i] : u32x4_t{0, 0, 0, 0};
+      const int row = idx / G::CPR;
+      uint8_t* dst = (is_v ? vring + (t % kSlots) * G::VTILE + row * G::VSTRIDE
+                           : kring + (t % kSlots) * G::KTILE + row * G::KSTRIDE) +
+                     (idx % G::CPR) * 16;
+      *reinterpret_cast<u32x4_t*>(dst) = t * kBN + row < N ? stg[i] : u32x4_t{0, 0, 0, 0};
     }
   };
 
@@ -179,43 +168,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // weights it was built from.
   float m_ref = kNegInf, d_lse = 0.f, d_out = 0.f;
 
+  // Per-lane fragment offsets (loop invariant). K operand: row swap23(l32) of the
+  // block, chunk 2c + half. V^T operand (transposing read): key 8*half + j/4 and
+  // head dims 16*((lane>>4)&1) + 4*(j%4) for lane j = lane % 16 of its group.
+  const int koff = swap23(l32) * G::KSTRIDE + half * 16;
+  const int voff = (8 * half + ((lane & 15) >> 2)) * G::VSTRIDE +
+                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
   // S^T block g (32 keys x this wavefront's 32 queries) from the K ring.
   auto qk = [&](int g) {
-    const uint8_t* ks = kring + ((g >> 1) % kSlots) * G::KTILE;
-    const int key = (g & 1) * 32 + swap23(l32);
-    const uint8_t* krow = ks + key * G::KROW;
-    const int sw = kswz(key);
+    const uint8_t* kb = kring + ((g >> 1) % kSlots) * G::KTILE + (g & 1) * 32 * G::KSTRIDE + koff;
     f32x16_t s = f32x16_t{};
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) {
-      const u32x4_t a = load16(krow + (((2 * c2 + half) ^ sw) << 4));
+      const u32x4_t a = load16(kb + 32 * c2);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[c2]), s, 0, 0, 0);
     }
     return s;
   };
-  // O^T += V^T (block g) P^T (block g). The A operand (rows = head dims 32db + l32,
-  // k = keys 16cc + 8*half + 0..7 of the block) comes from two transposing reads:
-  // lane j of each 16-lane group addresses key 4*r + j/4 (r = 0, 1) and head dims
-  // 4*(j%4) .. +3 of the group's 16 dims.
-  const int tr_key = (lane & 15) >> 2;
-  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // O^T += V^T (block g) P^T (block g). A operand rows: head dims 32db + l32; k:
+  // keys 16cc + 8*half + 0..7 of the block, from two transposing reads (r = 0, 1).
   auto pv = [&](int g, const uint32_t (&pk)[8]) {
-    const uint8_t* vs = vring + ((g >> 1) % kSlots) * G::KTILE;
+    const uint8_t* vb = vring + ((g >> 1) % kSlots) * G::VTILE + (g & 1) * 32 * G::VSTRIDE + voff;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const u32x4_t b = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) {
-        const int dim = 32 * db + tr_dim;
-        v4i16_t lo, hi;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int key = 32 * (g & 1) + 16 * cc + 8 * half + 4 * r + tr_key;
-          const int chunk = (dim >> 3) ^ vswz<D>(key);
-          const uint8_t* a = vs + key * G::KROW + (chunk << 4) + ((dim & 4) << 1);
-          const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a));
-          if (r == 0) lo = x; else hi = x;
-        }
+        const uint8_t* a0 = vb + 16 * cc * G::VSTRIDE + 64 * db;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0));
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0 + 4 * G::VSTRIDE));
         const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
         const u32x4_t a = {l2[0], l2[1], h2[0], h2[1]};
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b),
@@ -223,8 +206,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       }
     }
   };
-  // Softmax of block g against the reference maximum; returns the factor the
-  // accumulator must be multiplied by once block g-1 has been added (1 if unchanged).
   auto apply_mask = [&](int g, f32x16_t& s) {
     const int qi = qw0 + l32;
 #pragma unroll
@@ -233,6 +214,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       if (key >= N || (CAUSAL && key > qi)) s[r] = kNegInf;
     }
   };
+  // Softmax of block g against the reference maximum; returns the factor the
+  // accumulator must be multiplied by before block g is added (1 if unchanged).
   auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8]) {
     float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
@@ -277,6 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   f32x16_t s_cur = f32x16_t{};
   uint32_t p_prev[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float alpha_prev = 1.f;  // factor O owes the reference of the latest softmax
   if (nblk > 0) s_cur = qk(0);
 
   // One iteration per 32-key block; tiles (two blocks) are staged on even blocks
@@ -284,8 +268,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // the start of tile t, were last read during tile t-1.
   // A step is one basic block: QK of block g+1 (issued even past a wavefront's last
   // block, reading a resident slot, result unused), PV of block g-1 (at g = 0 with
-  // zero weights against tile 0) and the softmax of block g. The only branches are
-  // the mask of the diagonal / ragged block, applied first, and the rare rescale.
+  // zero weights against tile 0) and the softmax of block g. The only branches come
+  // first: the mask of the diagonal / ragged block and the rare rescale of O.
 #pragma unroll 1
   for (int g = 0; g < 2 * ntiles; ++g) {
     const int t = g >> 1;
@@ -293,15 +277,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if ((g & 1) == 0 && (tk >= 0 || tv >= 0)) gload(tk, tv);
     if (g < nblk) {
       if (needs_mask(g)) apply_mask(g, s_cur);
+      // Bring O to the reference block g-1 was weighted against, then add PV(g-1).
+      rescale(alpha_prev);
       uint32_t p_cur[8];
       const f32x16_t s_next = qk(g + 1);
       pv(g > 0 ? g - 1 : 0, p_prev);
-      const float alpha = softmax(s_cur, p_cur);
+      alpha_prev = softmax(s_cur, p_cur);
       s_cur = s_next;
-      rescale(alpha);
 #pragma unroll
       for (int i = 0; i < 8; ++i) p_prev[i] = p_cur[i];
-      if (g + 1 == nblk) pv(g, p_prev);  // last block: fold it in while V is resident
+      if (g + 1 == nblk) {  // last block: fold it in while its V tile is resident
+        rescale(alpha_prev);
+        pv(g, p_prev);
+      }
     }
     if (g & 1) {
       if (tk >= 0 || tv >= 0) lstore(tk, tv);
