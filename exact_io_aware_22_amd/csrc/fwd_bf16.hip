@@ -29,13 +29,18 @@
 //     given by swap23() below. P never leaves registers.
 //   * Each 32-key step g issues, in one basic block, the QK MFMAs of block g+1, the
 //     PV MFMAs of block g-1 and the softmax of block g, which are independent, so the
-//     hardware overlaps vector-ALU work with the matrix pipe.
-//   * K and V arrive 64 keys per tile through three-slot LDS rings (K two tiles
-//     ahead, V one tile ahead), copied global -> registers -> LDS by all threads
-//     (loads issued at the start of a tile, stores at its end), one barrier per
-//     tile. Both are row-major in LDS with padded rows (K: +16 bytes, V: +64 bytes),
-//     which keeps the fragment reads free of bank conflicts on 64 LDS banks and
-//     makes every fragment address one per-lane base plus a constant.
+//     hardware overlaps vector-ALU work with the matrix pipe. Scores and weights of
+//     consecutive steps live in alternating register sets (the loop body is one
+//     64-key tile, two steps), so nothing forces the softmax of block g ahead of the
+//     QK MFMAs that produce block g+1.
+//   * K and V arrive 64 keys per tile through three-slot LDS rings, copied global ->
+//     registers -> LDS by all threads, each load stored about one step later and no
+//     store right before the one barrier per tile. Both are row-major in LDS with
+//     padded rows (K: +16 bytes, V: +64 bytes), which keeps the fragment reads free
+//     of bank conflicts on 64 LDS banks; slot offsets are uniform scalars rotated
+//     once per tile, so every fragment address is one per-lane base plus a constant.
+//   * Tiles where nothing is masked, ragged or final run in a loop of their own with
+//     no branches but the rare rescale; the remaining tiles take the general loop.
 //   * The V^T operand of the PV MFMA is read with the transposing LDS read
 //     ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 //     (i mod 4) of what lane 4e + i/4 addressed, for e = 0..3, so lanes that address
@@ -124,33 +129,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kBM) - 1) >> 5) + 1) : nblk_all;
   const int ntiles = (nblk_wg + 1) >> 1;
 
-  // ---- staging: each thread copies SPT 16-byte chunks of a K tile and SPT of a V
-  // tile, global -> registers at the start of a tile, registers -> LDS at its end.
-  // Rows past the end of the sequence are stored as zeros, so masked keys meet
-  // finite values (zero weight times zero); the load itself reads the last row.
-  u32x4_t stg[2 * G::SPT];
-  auto gload = [&](int tk, int tv) {
+  // ---- staging: each thread copies SPT 16-byte chunks of a K or V tile, global ->
+  // registers, then registers -> LDS about one step later. Chunk i of a thread is
+  // column (tid % CPR) of row tid / CPR + i * RPP, so the global offsets are one
+  // loop-invariant lane offset plus constants off a uniform tile base. In the ragged
+  // last tile rows past the end of the sequence read the last row and are stored as
+  // zeros, so masked keys meet finite values (zero weight times zero).
+  constexpr int RPP = kThreads / G::CPR;  // rows per pass of all threads
+  const int srow = tid / G::CPR, scol = (tid % G::CPR) * 16;
+  const int goff = srow * D * 2 + scol;
+  const int kls = srow * G::KSTRIDE + scol, vls = srow * G::VSTRIDE + scol;
+  u32x4_t stg[G::SPT];
+  // full: the caller knows tile t lies inside the sequence (skips the ragged path).
+  auto gload = [&](const uint16_t* src, int t, bool full) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(src) + int64_t(t) * kBN * D * 2;
+    if (full || t * kBN + kBN <= N) {
 #pragma unroll
-    for (int i = 0; i < 2 * G::SPT; ++i) {
-      const bool is_v = i >= G::SPT;
-      const int idx = tid + kThreads * (i % G::SPT);
-      const int t = max(is_v ? tv : tk, 0);
-      const int gk = min(t * kBN + idx / G::CPR, N - 1);
-      stg[i] = load16((is_v ? Vh : Kh) + int64_t(gk) * D + (idx % G::CPR) * 8);
+      for (int i = 0; i < G::SPT; ++i) stg[i] = load16(base + goff + i * RPP * D * 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::SPT; ++i) {
+        const int gk = min(t * kBN + srow + i * RPP, N - 1);
+        stg[i] = load16(reinterpret_cast<const uint8_t*>(src) + int64_t(gk) * D * 2 + scol);
+      }
     }
   };
-  auto lstore = [&](int tk, int tv) {
+  auto lstore = [&](uint8_t* slot, int lane_off, int stride, int t, bool full) {
+    if (full || t * kBN + kBN <= N) {
 #pragma unroll
-    for (int i = 0; i < 2 * G::SPT; ++i) {
-      const bool is_v = i >= G::SPT;
-      const int t = is_v ? tv : tk;
-      if (t < 0) continue;
-      const int idx = tid + kThreads * (i % G::SPT);
-      const int row = idx / G::CPR;
-      uint8_t* dst = (is_v ? vring + (t % kSlots) * G::VTILE + row * G::VSTRIDE
-                           : kring + (t % kSlots) * G::KTILE + row * G::KSTRIDE) +
-                     (idx % G::CPR) * 16;
-      *reinterpret_cast<u32x4_t*>(dst) = t * kBN + row < N ? stg[i] : u32x4_t{0, 0, 0, 0};
+      for (int i = 0; i < G::SPT; ++i)
+        *reinterpret_cast<u32x4_t*>(slot + lane_off + i * RPP * stride) = stg[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::SPT; ++i)
+        *reinterpret_cast<u32x4_t*>(slot + lane_off + i * RPP * stride) =
+            t * kBN + srow + i * RPP < N ? stg[i] : u32x4_t{0, 0, 0, 0};
     }
   };
 
@@ -175,24 +188,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int voff = (8 * half + ((lane & 15) >> 2)) * G::VSTRIDE +
                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
-  // S^T block g (32 keys x this wavefront's 32 queries) from the K ring.
-  auto qk = [&](int g) {
-    const uint8_t* kb = kring + ((g >> 1) % kSlots) * G::KTILE + (g & 1) * 32 * G::KSTRIDE + koff;
+  // Fragments of S^T block g (32 keys x this wavefront's 32 queries): the K operand
+  // rows from the K ring, one 16-byte read per 16-wide chunk of the head dim.
+  // koff_blk / voff_blk: byte offset of a 32-key block in its ring (uniform).
+  auto kload = [&](int koff_blk, u32x4_t (&kf)[G::NCH]) {
+    const uint8_t* kb = kring + koff_blk + koff;
+#pragma unroll
+    for (int c2 = 0; c2 < G::NCH; ++c2) kf[c2] = load16(kb + 32 * c2);
+  };
+  auto qk = [&](const u32x4_t (&kf)[G::NCH]) {
     f32x16_t s = f32x16_t{};
 #pragma unroll
-    for (int c2 = 0; c2 < G::NCH; ++c2) {
-      const u32x4_t a = load16(kb + 32 * c2);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qf[c2]), s, 0, 0, 0);
-    }
+    for (int c2 = 0; c2 < G::NCH; ++c2)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c2]), as_bf16x8(qf[c2]), s, 0, 0, 0);
     return s;
   };
   // O^T += V^T (block g) P^T (block g). A operand rows: head dims 32db + l32; k:
-  // keys 16cc + 8*half + 0..7 of the block, from two transposing reads (r = 0, 1).
-  auto pv = [&](int g, const uint32_t (&pk)[8]) {
-    const uint8_t* vb = vring + ((g >> 1) % kSlots) * G::VTILE + (g & 1) * 32 * G::VSTRIDE + voff;
+  // keys 16cc + 8*half + 0..7 of the block, from two transposing reads.
+  auto vload = [&](int voff_blk, u32x4_t (&vf)[2 * G::NDB]) {
+    const uint8_t* vb = vring + voff_blk + voff;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const u32x4_t b = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
+    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) {
         const uint8_t* a0 = vb + 16 * cc * G::VSTRIDE + 64 * db;
@@ -200,10 +216,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         const v4i16_t hi =
             __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0 + 4 * G::VSTRIDE));
         const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-        const u32x4_t a = {l2[0], l2[1], h2[0], h2[1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b),
-                                                           oacc[db], 0, 0, 0);
+        vf[cc * G::NDB + db] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
       }
+  };
+  auto pv = [&](const u32x4_t (&vf)[2 * G::NDB], const uint32_t (&pk)[8]) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const u32x4_t b = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[cc * G::NDB + db]),
+                                                           as_bf16x8(b), oacc[db], 0, 0, 0);
     }
   };
   auto apply_mask = [&](int g, f32x16_t& s) {
@@ -247,54 +270,104 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       for (int db = 0; db < G::NDB; ++db) oacc[db] *= alpha;
     }
   };
-  auto needs_mask = [&](int g) { return (32 * g + 32 > N) || (CAUSAL && 32 * g + 31 > qw0); };
+  // Blocks from first_masked on need masking: the ragged tail (32g + 32 > N) and,
+  // causal, keys past this wavefront's first query (32g + 31 > qw0, qw0 a multiple of 32).
+  const int first_masked = CAUSAL ? min(N >> 5, qw0 >> 5) : (N >> 5);
 
-  // ---- prologue: K tiles 0 and 1, V tile 0
-  gload(0, 0);
-  lstore(0, 0);
+  // ---- prologue: K tiles 0 and 1 and V tile 0 in slots 0, 1, 0; V tile 1 loaded.
+  gload(Kh, 0, false);
+  lstore(kring, kls, G::KSTRIDE, 0, false);
+  gload(Vh, 0, false);
+  lstore(vring, vls, G::VSTRIDE, 0, false);
   if (ntiles > 1) {
-    gload(1, -1);
-    lstore(1, -1);
+    gload(Kh, 1, false);
+    lstore(kring + G::KTILE, kls, G::KSTRIDE, 1, false);
+    gload(Vh, 1, false);
   }
   __syncthreads();
 
-  f32x16_t s_cur = f32x16_t{};
-  uint32_t p_prev[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // Scores and weights alternate between two register sets from one step to the
+  // next (a, b), so the QK MFMAs of block g+1 never wait for the softmax of block g
+  // to release its scores, and no copies are made.
+  f32x16_t sa = f32x16_t{}, sb = f32x16_t{};
+  uint32_t pa[8] = {0, 0, 0, 0, 0, 0, 0, 0}, pb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;  // factor O owes the reference of the latest softmax
-  if (nblk > 0) s_cur = qk(0);
+  u32x4_t kf[G::NCH], vf[2 * G::NDB];
+  if (nblk > 0) {
+    kload(0, kf);
+    sa = qk(kf);
+  }
 
-  // One iteration per 32-key block; tiles (two blocks) are staged on even blocks
-  // and published after odd ones. Slots (t+2)%3 of K and (t+1)%3 of V, refilled at
-  // the start of tile t, were last read during tile t-1.
-  // A step is one basic block: QK of block g+1 (issued even past a wavefront's last
-  // block, reading a resident slot, result unused), PV of block g-1 (at g = 0 with
-  // zero weights against tile 0) and the softmax of block g. The only branches come
-  // first: the mask of the diagonal / ragged block and the rare rescale of O.
+  // Step g: scores of block g in s_in, weights of block g-1 in p_in; K block g+1 at
+  // kblk, V block g-1 at vblk. One basic block issues QK of block g+1 (issued even
+  // past a wavefront's last block, reading a resident slot, result unused), PV of
+  // block g-1 (at g = 0 with zero weights against block 0) and the softmax of block
+  // g. The only branches come first: the mask of the diagonal / ragged block and the
+  // rare rescale of O.
+  auto step = [&](int g, int kblk, int vblk, f32x16_t& s_in, f32x16_t& s_out,
+                  const uint32_t (&p_in)[8], uint32_t (&p_out)[8], bool unmasked) {
+    if (!unmasked && g >= first_masked) apply_mask(g, s_in);
+    // Bring O to the reference block g-1 was weighted against, then add PV(g-1).
+    rescale(alpha_prev);
+    kload(kblk, kf);
+    s_out = qk(kf);
+    vload(vblk, vf);
+    pv(vf, p_in);
+    alpha_prev = softmax(s_in, p_out);
+  };
+
+  // One iteration per tile t (blocks 2t and 2t+1). Slot offsets of K tiles t, t+1,
+  // t+2 and of V tiles t-1, t, t+1 rotate through the three slots of each ring.
+  // Staging within tile t: V tile t+1 (loaded during tile t-1) is stored first and K
+  // tile t+2 loaded; after the first step K tile t+2 is stored and V tile t+2 loaded.
+  // During tile t the steps read K tiles t, t+1 and V tiles t-1, t, so the slots
+  // written (those of K tile t-1 and V tile t-2) were last read before the barrier
+  // that ended tile t-1, and what is written is first read after the barrier that
+  // ends tile t. No store sits right before a barrier.
+  int ks0 = 0, ks1 = G::KTILE, ks2 = 2 * G::KTILE;
+  int vsp = 2 * G::VTILE, vs0 = 0, vs1 = G::VTILE;
+  constexpr int KH = 32 * G::KSTRIDE, VH = 32 * G::VSTRIDE;  // second block of a tile
+  auto rotate = [&]() {
+    const int k0 = ks0, v0 = vsp;
+    ks0 = ks1; ks1 = ks2; ks2 = k0;
+    vsp = vs0; vs0 = vs1; vs1 = v0;
+  };
+  // Steady tiles [0, t_steady): both steps run unmasked, the wavefront's last block
+  // lies beyond the tile, and the tiles staged during it (t+1, t+2) are full, so the
+  // body needs no branch but the rescale. Every wavefront passes one barrier per tile
+  // in either loop, so the counts match across the workgroup.
+  const int last_free = min(first_masked, nblk - 1);  // blocks [0, last_free) plain
+  const int t_steady = max(0, min(min(last_free >> 1, ntiles - 2), (N >> 6) - 2));
+  int t = 0;
 #pragma unroll 1
-  for (int g = 0; g < 2 * ntiles; ++g) {
-    const int t = g >> 1;
-    const int tk = t + 2 < ntiles ? t + 2 : -1, tv = t + 1 < ntiles ? t + 1 : -1;
-    if ((g & 1) == 0 && (tk >= 0 || tv >= 0)) gload(tk, tv);
-    if (g < nblk) {
-      if (needs_mask(g)) apply_mask(g, s_cur);
-      // Bring O to the reference block g-1 was weighted against, then add PV(g-1).
+  for (; t < t_steady; ++t) {
+    lstore(vring + vs1, vls, G::VSTRIDE, t + 1, true);
+    gload(Kh, t + 2, true);
+    step(2 * t, ks0 + KH, t > 0 ? vsp + VH : vs0, sa, sb, pa, pb, true);
+    lstore(kring + ks2, kls, G::KSTRIDE, t + 2, true);
+    gload(Vh, t + 2, true);
+    step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, true);
+    __syncthreads();
+    rotate();
+  }
+#pragma unroll 1
+  for (; t < ntiles; ++t) {
+    if (t + 1 < ntiles) lstore(vring + vs1, vls, G::VSTRIDE, t + 1, false);
+    if (t + 2 < ntiles) gload(Kh, t + 2, false);
+    if (2 * t < nblk) step(2 * t, ks0 + KH, t > 0 ? vsp + VH : vs0, sa, sb, pa, pb, false);
+    if (t + 2 < ntiles) {
+      lstore(kring + ks2, kls, G::KSTRIDE, t + 2, false);
+      gload(Vh, t + 2, false);
+    }
+    if (2 * t + 1 < nblk) step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, false);
+    if (nblk - 1 == 2 * t || nblk - 1 == 2 * t + 1) {
+      // This wavefront's last block is in tile t: fold it in while its V is resident.
       rescale(alpha_prev);
-      uint32_t p_cur[8];
-      const f32x16_t s_next = qk(g + 1);
-      pv(g > 0 ? g - 1 : 0, p_prev);
-      alpha_prev = softmax(s_cur, p_cur);
-      s_cur = s_next;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p_prev[i] = p_cur[i];
-      if (g + 1 == nblk) {  // last block: fold it in while its V tile is resident
-        rescale(alpha_prev);
-        pv(g, p_prev);
-      }
+      vload(vs0 + ((nblk & 1) ? 0 : VH), vf);
+      pv(vf, (nblk & 1) ? pb : pa);
     }
-    if (g & 1) {
-      if (tk >= 0 || tv >= 0) lstore(tk, tv);
-      __syncthreads();
-    }
+    __syncthreads();
+    rotate();
   }
 
   // ---- read out: o / d once, lse = ln(sum) = (r c + log2 d) ln 2
