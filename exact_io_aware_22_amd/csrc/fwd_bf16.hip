@@ -12,8 +12,10 @@
 // (m, d, o) and (r, d e^{m-r}, o e^{m-r}) are the same state in other coordinates
 // (section "Twisted Monoid": the combine is transported by any bijection). The kernel
 // keeps r fixed until a new block's maximum exceeds it by more than 2^kTau in
-// weight, so weights stay in [0, 2^kTau] (no overflow, same relative precision) and
-// the accumulator is rescaled only on those rare steps instead of every block. O is
+// weight, so weights stay in [0, 2^kTau] and the accumulator is rescaled only on
+// those rare steps instead of every block. Floating point keeps the same relative
+// precision at any magnitude, and with kTau = 32 the sums stay far inside float32
+// range (d <= N 2^32; |o| <= N 2^32 max|v|) for any sequence length an int holds. O is
 // normalised by the sum of the weights as rounded to bf16 for the PV product, so it
 // is divided by exactly the weights it was built from; the log-sum-exp uses the
 // float32 sum.
@@ -60,7 +62,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per LDS tile (two 32-key blocks)
 constexpr int kSlots = 3;         // LDS ring depth for K and for V
-constexpr float kTau = 8.0f;      // rescale when the maximum grows by more than 2^8
+constexpr float kTau = 32.0f;     // rescale when the maximum grows by more than 2^32
 
 // Row r of a 32-row K operand block holds key swap23(r): bits 2 and 3 exchanged.
 // With this order the accumulator registers 8c..8c+7 of a lane hold 8 consecutive

@@ -179,6 +179,25 @@ def test_single_key_and_row_zero():
     np.testing.assert_allclose(lse, s, atol=1e-4, rtol=0)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_growing_scores_force_rescales(D, causal):
+    """Scores that climb steeply along the keys: each 32-key block's maximum exceeds
+    the previous one by about 2^40 in weight, so the running maximum moves on every
+    block and the accumulator is rescaled every step (the reference-maximum change
+    of coordinates, exercised on every step instead of rarely)."""
+    N = 333
+    q = random_tensor((1, 2, N, D), 21, torch.bfloat16)
+    k = random_tensor((1, 2, N, D), 22, torch.bfloat16)
+    v = random_tensor((1, 2, N, D), 23, torch.bfloat16)
+    q[..., 0] = 1.0
+    k[..., 0] = (10.0 * torch.arange(N, dtype=torch.float32)).to(torch.bfloat16)
+    scale = 1 / math.sqrt(D)
+    o, lse = run_forward(q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal)
+    check(o, lse, o_ref, lse_ref, torch.bfloat16, f"growing scores D={D} causal={causal}")
+
+
 def test_row_shift_invariance_fp32():
     N, D = 200, 64
     q = random_tensor((1, 1, N, D), 10, torch.float32)
