@@ -9,8 +9,8 @@ keys, D=128, 64 chunks of 512) as HBM GB/s, the other prefill workloads' rates,
 a live roofline of the dominant kernel, a sampled parity check of the timed
 outputs against the fp64 oracle, and the oracle itself timed on the host cores.
 
-Timing: inputs are resident in HBM before the timed region; W untimed warm-up
-steps, then K steps bracketed by torch.cuda.synchronize() and HIP events recorded
+Timing: inputs are resident in HBM before the timed region; at least W untimed
+warm-up steps and at least 0.25 s of them, then K steps bracketed by torch.cuda.synchronize() and HIP events recorded
 on the stream the kernels are launched on.
 """
 from __future__ import annotations
@@ -64,10 +64,21 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+WARM_SECONDS = 0.25  # the clock ramps up over the first tens of milliseconds of load
+
+
 def time_launches(fn, steps: int, warmup: int, torch):
-    """Average milliseconds per call of fn(), HIP events on the current stream."""
-    for _ in range(warmup):
+    """Average milliseconds per call of fn(), HIP events on the current stream.
+
+    Warm-up runs at least `warmup` calls and at least WARM_SECONDS of them, so a short
+    kernel measured after an idle stretch is not timed on a cold clock."""
+    t_end = time.perf_counter() + WARM_SECONDS
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)

@@ -11,14 +11,16 @@
 // Reference maximum. Any reference value r may stand in for the running maximum m:
 // (m, d, o) and (r, d e^{m-r}, o e^{m-r}) are the same state in other coordinates
 // (section "Twisted Monoid": the combine is transported by any bijection). The kernel
-// keeps r fixed until a new block's maximum exceeds it by more than 2^kTau in
-// weight, so weights stay in [0, 2^kTau] and the accumulator is rescaled only on
-// those rare steps instead of every block. Floating point keeps the same relative
-// precision at any magnitude, and with kTau = 32 the sums stay far inside float32
-// range (d <= N 2^32; |o| <= N 2^32 max|v|) for any sequence length an int holds. O is
-// normalised by the sum of the weights as rounded to bf16 for the PV product, so it
-// is divided by exactly the weights it was built from; the log-sum-exp uses the
-// float32 sum.
+// weights each block against the current r straight away and keeps r until some
+// weight would exceed 2^kTau (checked on each lane's block sum, after the fact); only
+// then is the block's maximum taken as the new r and the block weighted again. So
+// weights stay in [0, 2^kTau], no maximum is computed on ordinary steps, and the
+// accumulator is rescaled only on those rare steps instead of every block. Floating
+// point keeps the same relative precision at any magnitude, and with kTau = 32 the
+// sums stay far inside float32 range (d <= N 2^32; |o| <= N 2^32 max|v|) for any
+// sequence length an int holds. O is normalised by the sum of the weights as rounded
+// to bf16 for the PV product, so it is divided by exactly the weights it was built
+// from; the log-sum-exp uses the float32 sum.
 //
 // Work decomposition (one workgroup = 8 wavefronts = 256 query rows of one head):
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -63,6 +65,8 @@ constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per LDS tile (two 32-key blocks)
 constexpr int kSlots = 3;         // LDS ring depth for K and for V
 constexpr float kTau = 32.0f;     // rescale when the maximum grows by more than 2^32
+constexpr float kSumLimit = 4294967296.0f;  // 2^kTau
+constexpr float kInf = __builtin_inff();
 
 // Row r of a 32-row K operand block holds key swap23(r): bits 2 and 3 exchanged.
 // With this order the accumulator registers 8c..8c+7 of a lane hold 8 consecutive
@@ -182,6 +186,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // weights as rounded to bf16 for the PV MFMA, so O is normalised by exactly the
   // weights it was built from.
   float m_ref = kNegInf, d_lse = 0.f, d_out = 0.f;
+  float nmc_ref = kInf;  // -m_ref * c; +inf while there is no reference yet
 
   // Per-lane fragment offsets (loop invariant). K operand: row swap23(l32) of the
   // block, chunk 2c + half. V^T operand (transposing read): key 8*half + j/4 and
@@ -241,18 +246,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   };
   // Softmax of block g against the reference maximum; returns the factor the
   // accumulator must be multiplied by before block g is added (1 if unchanged).
-  auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8]) {
-    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-    mx = fmaxf(mx, s[15]);
-    mx = halves_max(mx);
-    const bool grow = (mx - m_ref) * c > kTau;  // false when both are -inf
-    const float m_new = grow ? mx : m_ref;
-    const float alpha = grow ? exp2_hw((m_ref - m_new) * c) : 1.f;
-    const float nmc = m_new == kNegInf ? 0.f : -m_new * c;
-    float ps = 0.f, pq = 0.f;
+  // Weights of one block against the reference, packed to bf16 for the PV MFMA, with
+  // their float32 sum (ps) and the sum of the packed values (pq).
+  auto weights = [&](const f32x16_t& s, float nmc, uint32_t (&pk)[8], float& ps, float& pq) {
     const bf16x2_t ones = as_bf16x2(0x3f803f80u);
+    ps = 0.f;
+    pq = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p0 = exp2_hw(fmaf(s[2 * i], c, nmc));
@@ -261,9 +260,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       pk[i] = pack_bf16x2(p0, p1);
       pq = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[i]), ones, pq, false);
     }
+  };
+  // The block is weighted against the current reference straight away; only if some
+  // lane's 16 weights sum past 2^kTau (which also catches +inf, NaN and the first
+  // block, whose reference is -inf) does the wavefront take the rare path: the
+  // block's maximum becomes the reference, O owes the factor alpha, and the block is
+  // weighted again. No weight above 2^kTau is ever kept.
+  auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8]) {
+    float ps, pq, alpha = 1.f;
+    weights(s, nmc_ref, pk, ps, pq);
+    if (__builtin_amdgcn_ballot_w64(!(ps <= kSumLimit))) {
+      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+      mx = halves_max(fmaxf(mx, s[15]));
+      const float m_new = fmaxf(m_ref, mx);
+      alpha = m_ref == kNegInf ? 1.f : exp2_hw((m_ref - m_new) * c);
+      m_ref = m_new;
+      // A row with no visible key yet keeps +inf, so its first finite score comes
+      // back here; its masked scores get weight exp2(-inf) = 0 below.
+      nmc_ref = m_new == kNegInf ? kInf : -m_new * c;
+      weights(s, m_new == kNegInf ? 0.f : nmc_ref, pk, ps, pq);
+    }
     d_lse = fmaf(d_lse, alpha, ps);
     d_out = fmaf(d_out, alpha, pq);
-    m_ref = m_new;
     return alpha;
   };
   auto rescale = [&](float alpha) {
