@@ -37,9 +37,9 @@
 //     consecutive steps live in alternating register sets (the loop body is one
 //     64-key tile, two steps), so nothing forces the softmax of block g ahead of the
 //     QK MFMAs that produce block g+1.
-//   * K and V arrive 64 keys per tile through three-slot LDS rings, copied global ->
-//     registers -> LDS by all threads, each load stored about one step later and no
-//     store right before the one barrier per tile. Both are row-major in LDS with
+//   * K and V arrive 64 keys per tile through three-slot LDS rings by direct global ->
+//     LDS loads (global_load_lds_dwordx4, no register staging), issued two steps
+//     before the one barrier per tile that publishes them. Both are row-major in LDS with
 //     padded rows (K: +16 bytes, V: +64 bytes), which keeps the fragment reads free
 //     of bank conflicts on 64 LDS banks; slot offsets are uniform scalars rotated
 //     once per tile, so every fragment address is one per-lane base plus a constant.
@@ -88,7 +88,6 @@ struct Geo {
   static constexpr int KTILE = kBN * KSTRIDE;
   static constexpr int VTILE = kBN * VSTRIDE;
   static constexpr int LDS = kSlots * (KTILE + VTILE);
-  static constexpr int SPT = kBN * CPR / kThreads;  // chunks of a tile per thread
 };
 
 // Workgroup -> (head, query tile). Workgroups are dispatched round-robin over the
@@ -135,43 +134,55 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kBM) - 1) >> 5) + 1) : nblk_all;
   const int ntiles = (nblk_wg + 1) >> 1;
 
-  // ---- staging: each thread copies SPT 16-byte chunks of a K or V tile, global ->
-  // registers, then registers -> LDS about one step later. Chunk i of a thread is
-  // column (tid % CPR) of row tid / CPR + i * RPP, so the global offsets are one
-  // loop-invariant lane offset plus constants off a uniform tile base. In the ragged
-  // last tile rows past the end of the sequence read the last row and are stored as
-  // zeros, so masked keys meet finite values (zero weight times zero).
-  constexpr int RPP = kThreads / G::CPR;  // rows per pass of all threads
-  const int srow = tid / G::CPR, scol = (tid % G::CPR) * 16;
-  const int goff = srow * D * 2 + scol;
-  const int kls = srow * G::KSTRIDE + scol, vls = srow * G::VSTRIDE + scol;
-  u32x4_t stg[G::SPT];
-  // full: the caller knows tile t lies inside the sequence (skips the ragged path).
-  auto gload = [&](const uint16_t* src, int t, bool full) {
+  // ---- staging by direct global -> LDS loads (global_load_lds_dwordx4): one such
+  // load moves 64 lanes x 16 bytes to 1 KB of consecutive LDS at M0 + 16 * lane. A
+  // padded ring tile is exactly CK (K) or CV (V) such kilobytes, so each kilobyte j
+  // is one load in which lane i fills LDS chunk 64 j + i, i.e. row (64 j + i) / C and
+  // column (64 j + i) % C of the padded tile; pad columns take a copy of column
+  // CPR - 1 and are never read. Wavefront w issues kilobytes w, w + 8, w + 16. In the
+  // ragged last tile, rows past the end of the sequence take a copy of the last row
+  // (finite, so masked keys still meet zero weight times a finite value).
+  // The loads are issued from inline assembly so that the compiler, which does not
+  // see them write LDS, inserts no waits before the fragment reads; the code waits
+  // for them itself (vmcnt) before the barrier that publishes a tile. The compiler
+  // makes no use of M0 in this kernel, which the assembly sets for each load.
+  constexpr int CK = G::KSTRIDE / 16, CV = G::VSTRIDE / 16;  // chunks per padded row
+  constexpr int MAXI = (CV + kWaves - 1) / kWaves;            // loads per wave per tile
+  static_assert(CK <= CV && G::KTILE == CK * 1024 && G::VTILE == CV * 1024, "tile = C KB");
+  auto chunk_off = [&](int j, int C, int t, bool full) -> uint32_t {
+    const int p = 64 * j + lane, r = p / C, col = min(p % C, G::CPR - 1);
+    const int row = full ? r : min(t * kBN + r, N - 1) - t * kBN;
+    return uint32_t(row * D * 2 + col * 16);
+  };
+  uint32_t dk[MAXI], dv[MAXI];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    dk[i] = chunk_off(wave + kWaves * i, CK, 0, true);
+    dv[i] = chunk_off(wave + kWaves * i, CV, 0, true);
+  }
+  auto dma = [&](const uint16_t* src, uint8_t* slot, int C, const uint32_t (&d)[MAXI], int t,
+                 bool full) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(src) + int64_t(t) * kBN * D * 2;
-    if (full || t * kBN + kBN <= N) {
+    const bool ragged = !full && t * kBN + kBN > N;
+    const uint32_t lds0 =
+        uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(uint8_t, slot)));
 #pragma unroll
-      for (int i = 0; i < G::SPT; ++i) stg[i] = load16(base + goff + i * RPP * D * 2);
-    } else {
-#pragma unroll
-      for (int i = 0; i < G::SPT; ++i) {
-        const int gk = min(t * kBN + srow + i * RPP, N - 1);
-        stg[i] = load16(reinterpret_cast<const uint8_t*>(src) + int64_t(gk) * D * 2 + scol);
+    for (int i = 0; i < MAXI; ++i) {
+      const int j = wave + kWaves * i;
+      if (j < C) {
+        const uint32_t off = ragged ? chunk_off(j, C, t, false) : d[i];
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(m0), "v"(off), "s"(base)
+                     : "memory");
       }
     }
   };
-  auto lstore = [&](uint8_t* slot, int lane_off, int stride, int t, bool full) {
-    if (full || t * kBN + kBN <= N) {
-#pragma unroll
-      for (int i = 0; i < G::SPT; ++i)
-        *reinterpret_cast<u32x4_t*>(slot + lane_off + i * RPP * stride) = stg[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < G::SPT; ++i)
-        *reinterpret_cast<u32x4_t*>(slot + lane_off + i * RPP * stride) =
-            t * kBN + srow + i * RPP < N ? stg[i] : u32x4_t{0, 0, 0, 0};
-    }
-  };
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued through the
+  // builtin, not assembly, so the compiler's own wait bookkeeping also learns that
+  // every vector-memory load (the Q fragments included) has completed.
+  auto dma_wait = []() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   // ---- per-lane state: Q^T fragments, O^T accumulator, reference max r, d
   const int qrow = qw0 + l32;
@@ -297,15 +308,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int first_masked = CAUSAL ? min(N >> 5, qw0 >> 5) : (N >> 5);
 
   // ---- prologue: K tiles 0 and 1 and V tile 0 in slots 0, 1, 0; V tile 1 loaded.
-  gload(Kh, 0, false);
-  lstore(kring, kls, G::KSTRIDE, 0, false);
-  gload(Vh, 0, false);
-  lstore(vring, vls, G::VSTRIDE, 0, false);
-  if (ntiles > 1) {
-    gload(Kh, 1, false);
-    lstore(kring + G::KTILE, kls, G::KSTRIDE, 1, false);
-    gload(Vh, 1, false);
-  }
+  dma(Kh, kring, CK, dk, 0, false);
+  dma(Vh, vring, CV, dv, 0, false);
+  if (ntiles > 1) dma(Kh, kring + G::KTILE, CK, dk, 1, false);
+  dma_wait();
   __syncthreads();
 
   // Scores and weights alternate between two register sets from one step to the
@@ -340,12 +346,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   // One iteration per tile t (blocks 2t and 2t+1). Slot offsets of K tiles t, t+1,
   // t+2 and of V tiles t-1, t, t+1 rotate through the three slots of each ring.
-  // Staging within tile t: V tile t+1 (loaded during tile t-1) is stored first and K
-  // tile t+2 loaded; after the first step K tile t+2 is stored and V tile t+2 loaded.
-  // During tile t the steps read K tiles t, t+1 and V tiles t-1, t, so the slots
-  // written (those of K tile t-1 and V tile t-2) were last read before the barrier
-  // that ended tile t-1, and what is written is first read after the barrier that
-  // ends tile t. No store sits right before a barrier.
+  // Tile t opens by issuing the direct loads of K tile t+2 and V tile t+1 and closes
+  // by waiting for them before its barrier, so they have two steps to land. During
+  // tile t the steps read K tiles t, t+1 and V tiles t-1, t, so the slots written
+  // (those of K tile t-1 and V tile t-2) were last read before the barrier that ended
+  // tile t-1, and what is written is first read after the barrier that ends tile t.
   int ks0 = 0, ks1 = G::KTILE, ks2 = 2 * G::KTILE;
   int vsp = 2 * G::VTILE, vs0 = 0, vs1 = G::VTILE;
   constexpr int KH = 32 * G::KSTRIDE, VH = 32 * G::VSTRIDE;  // second block of a tile
@@ -363,24 +368,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   int t = 0;
 #pragma unroll 1
   for (; t < t_steady; ++t) {
-    lstore(vring + vs1, vls, G::VSTRIDE, t + 1, true);
-    gload(Kh, t + 2, true);
+    dma(Kh, kring + ks2, CK, dk, t + 2, true);
+    dma(Vh, vring + vs1, CV, dv, t + 1, true);
     step(2 * t, ks0 + KH, t > 0 ? vsp + VH : vs0, sa, sb, pa, pb, true);
-    lstore(kring + ks2, kls, G::KSTRIDE, t + 2, true);
-    gload(Vh, t + 2, true);
     step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, true);
+    dma_wait();
     __syncthreads();
     rotate();
   }
 #pragma unroll 1
   for (; t < ntiles; ++t) {
-    if (t + 1 < ntiles) lstore(vring + vs1, vls, G::VSTRIDE, t + 1, false);
-    if (t + 2 < ntiles) gload(Kh, t + 2, false);
+    if (t + 2 < ntiles) dma(Kh, kring + ks2, CK, dk, t + 2, false);
+    if (t + 1 < ntiles) dma(Vh, vring + vs1, CV, dv, t + 1, false);
     if (2 * t < nblk) step(2 * t, ks0 + KH, t > 0 ? vsp + VH : vs0, sa, sb, pa, pb, false);
-    if (t + 2 < ntiles) {
-      lstore(kring + ks2, kls, G::KSTRIDE, t + 2, false);
-      gload(Vh, t + 2, false);
-    }
     if (2 * t + 1 < nblk) step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, false);
     if (nblk - 1 == 2 * t || nblk - 1 == 2 * t + 1) {
       // This wavefront's last block is in tile t: fold it in while its V is resident.
@@ -388,6 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       vload(vs0 + ((nblk & 1) ? 0 : VH), vf);
       pv(vf, (nblk & 1) ? pb : pa);
     }
+    dma_wait();
     __syncthreads();
     rotate();
   }
