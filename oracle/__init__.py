@@ -1,4 +1,4 @@
-"""fp64 CPU oracle (test infrastructure only; see oracle.fp64)."""
+"""fp64 CPU oracle (test infrastructure only; see oracle.fp64 and oracle.backward)."""
 from .fp64 import (  # noqa: F401
     LOG2E,
     NEG_INF,
@@ -16,3 +16,4 @@ from .fp64 import (  # noqa: F401
     safe_softmax_rows,
     split_bounds,
 )
+from .backward import attention_backward  # noqa: F401,E402
