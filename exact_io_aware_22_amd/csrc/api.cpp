@@ -39,7 +39,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape: negative size, D not 64 or 128, splits < 1, or too large";
     case FA_ERR_DTYPE: return "unsupported dtype (expected FA_F32 or FA_BF16)";
-    case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, m/d/lse 4-byte alignment)";
+    case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, m/d/lse/delta 4-byte alignment)";
     case FA_ERR_ARG: return "invalid argument: scale must be finite and > 0, causal 0 or 1";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     default: return "unknown fa error code";
@@ -80,6 +80,23 @@ int fa_decode_partials(const void* q, const void* k, const void* v, float* m, fl
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(dtype == FA_BF16 ? fa::launch_decode_partials_bf16(a, s)
                                      : fa::launch_decode_partials_f32(a, s));
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* delta, float* dq, float* dk, float* dv, int B, int H,
+                int N, int D, float scale, int causal, int dtype, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || !head_dim_ok(D) || !count_ok(B, H, N, D)) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;  // empty: no pointer is touched
+  if (!q || !k || !v || !o || !lse || !dout || !delta || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(delta, 4))
+    return FA_ERR_ALIGN;
+  fa::BwdArgs a{q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, D, scale, causal == 1};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(dtype == FA_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f32(a, s));
 }
 
 int fa_combine_partials(const float* m, const float* d, const float* o_part, int splits,

@@ -1,0 +1,465 @@
+// Exact attention backward, bfloat16 inputs, float32 accumulation, on gfx950 MFMA.
+//
+// The pages name the backward pass that recomputes attention instead of storing it,
+// keeping only the per-row log-sum-exp of the forward ("Learning FlashAttention the
+// Hard Way -- Part 1", its topic list), but print no formula. The gradients follow
+// by the chain rule from the forward definition (section "FlashAttention: Not So
+// Special": S = scale Q K^T, P = row softmax(S), O = P V). With lse from the forward,
+// P_ij = e^{S_ij - lse_i} = 2^{S_ij c - lse_i log2 e}, c = scale log2 e (section
+// "Alternative Twist: Base 2"), and for an upstream gradient dO:
+//   dV = P^T dO,  dP = dO V^T,  Delta_i = sum_d dO_id O_id (= sum_j P_ij dP_ij),
+//   dS = P (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+// Masked keys have P = 0 and contribute nothing.
+//
+// Three kernels:
+//   * delta_kernel: Delta_i from dO (bf16) and the forward's O (fp32), 16 lanes per row.
+//   * dq_kernel: a wavefront owns 32 query rows (Q^T and dO^T fragments in registers)
+//     and walks the key tiles: S^T = K Q^T and dP^T = V dO^T (A operands: K and V rows
+//     from LDS), P^T and dS^T element-wise (one lse and one Delta per lane), then
+//     dQ^T += K^T dS^T with K^T read by the transposing LDS read.
+//   * dkdv_kernel: a wavefront owns 32 key rows (K^T and V^T fragments in registers)
+//     and walks the query tiles: S = Q K^T and dP = dO V^T (A operands: Q and dO rows
+//     from LDS), P and dS element-wise (16 queries per lane, their lse and Delta read
+//     from LDS), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by the
+//     transposing LDS read.
+// Every product is v_mfma_f32_32x32x16_bf16; the element-wise results a lane holds
+// are, after bf16 packing, exactly the B operand of the next product (the swap23 row
+// order used by the forward kernel). A tile read both row-wise (16-byte reads) and
+// column-wise (transposing reads) is stored twice in LDS, with +16-byte rows for the
+// former and +64-byte rows for the latter: each padding keeps its own read pattern
+// free of bank conflicts on 64 banks, and no single padding serves both.
+#include "device.h"
+#include "launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kWavesB = 4;                 // wavefronts per workgroup (one per SIMD)
+constexpr int kThreadsB = 64 * kWavesB;
+constexpr int kRowsB = 32 * kWavesB;       // rows a workgroup owns (queries or keys)
+constexpr int kTile = 64;                  // rows per LDS tile (two 32-row blocks)
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+#define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Row r of a 32-row A operand holds row swap23(r) (bits 2 and 3 exchanged), so a
+// lane's accumulator registers 8c..8c+7 hold 8 consecutive rows 16c + 8 half + i.
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <int D>
+struct BGeo {
+  static constexpr int NCH = D / 16;       // 16-wide k chunks of the head dim
+  static constexpr int NDB = D / 32;       // 32-row blocks of a transposed accumulator
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int RS = D * 2 + 16;    // row stride, row-read copy
+  static constexpr int CS = D * 2 + 64;    // row stride, transposing-read copy
+  static constexpr int RT = kTile * RS;
+  static constexpr int CT = kTile * CS;
+  static constexpr int SPT = kTile * CPR / kThreadsB;  // 16-byte chunks per thread per tile
+};
+
+// Per-lane offsets of the two fragment read patterns (see the forward kernel):
+// row reads: row swap23(l32) of a 32-row block, chunk 2c + half at +32 c bytes;
+// transposing reads: rows 8 half + (lane & 15) / 4, head dims 16 ((lane >> 4) & 1) +
+// 4 (lane & 3); block (cc, db) at +16 cc CS + 64 db, high half at +4 CS.
+__device__ __forceinline__ int row_off(int lane, int RS) {
+  return swap23(lane & 31) * RS + (lane >> 5) * 16;
+}
+__device__ __forceinline__ int tr_off(int lane, int CS) {
+  return (8 * (lane >> 5) + ((lane & 15) >> 2)) * CS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+}
+
+// A operand of rows [32 block] (row reads), k chunk c2.
+__device__ __forceinline__ bf16x8_t frag_row(const uint8_t* base, int c2) {
+  return as_bf16x8(load16(base + 32 * c2));
+}
+// A operand of the transposed block (head dims 32 db.., rows 16 cc + 8 half + 0..7).
+__device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* base, int cc, int db, int CS) {
+  const uint8_t* a0 = base + 16 * cc * CS + 64 * db;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0 + 4 * CS));
+  const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+  return as_bf16x8(u32x4_t{l2[0], l2[1], h2[0], h2[1]});
+}
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroup -> (head, tile): all tiles of a head on one XCD, heaviest first.
+// heavy_last_tile: causal dq (the last query tiles see the most keys); otherwise causal
+// dk/dv (the first key tiles see the most queries).
+__device__ __forceinline__ void map_bwd(int bid, int BH, int ntile, bool causal, bool heavy_last,
+                                        int& bh, int& t) {
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7, slot = bid >> 3, hpx = BH >> 3;
+    bh = (slot % hpx) * 8 + xcd;
+    t = slot / hpx;
+  } else {
+    bh = bid % BH;
+    t = bid / BH;
+  }
+  if (causal && heavy_last) t = ntile - 1 - t;
+}
+
+// ------------------------------------------------------------------ Delta
+// Delta_i = sum_d dO_id O_id; 16 lanes per row, D / 16 elements per lane.
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ dO,
+                                                    const float* __restrict__ O,
+                                                    float* __restrict__ delta, int64_t rows) {
+  constexpr int E = D / 16;
+  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint16_t* g = dO + row * D + part * E;
+    const float* o = O + row * D + part * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(g + e);
+      acc = fmaf(bf16_lo(w), o[e], acc);
+      acc = fmaf(bf16_hi(w), o[e + 1], acc);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && part == 0) delta[row] = acc;
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreadsB, 1) void dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ dQ,
+    int N, int BH, int nqt, float c, float scale) {
+  using G = BGeo<D>;
+  constexpr int SLOT = 2 * G::RT + G::CT;  // K rows, K transposing copy, V rows
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  int bh, qt;
+  map_bwd(blockIdx.x, BH, nqt, CAUSAL, true, bh, qt);
+  const int64_t head = int64_t(bh) * N * D;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  const int q0 = qt * kRowsB, qw0 = q0 + 32 * wave, qrow = qw0 + l32;
+
+  const int nblk_all = (N + 31) >> 5;
+  const int nblk = qw0 >= N ? 0 : (CAUSAL ? min(nblk_all, (qw0 >> 5) + 1) : nblk_all);
+  const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kRowsB) - 1) >> 5) + 1) : nblk_all;
+  const int ntiles = (nblk_wg + 1) >> 1;
+
+  // Own rows: Q^T and dO^T as B operands (k = head dims 16 c2 + 8 half + 0..7).
+  u32x4_t qf[G::NCH], df[G::NCH];
+  float lse2 = kInfB, dl = 0.f;
+  {
+    const bool ok = qrow < N;
+#pragma unroll
+    for (int c2 = 0; c2 < G::NCH; ++c2) {
+      qf[c2] = ok ? load16(Q + head + int64_t(qrow) * D + 16 * c2 + 8 * half) : u32x4_t{0, 0, 0, 0};
+      df[c2] = ok ? load16(dO + head + int64_t(qrow) * D + 16 * c2 + 8 * half) : u32x4_t{0, 0, 0, 0};
+    }
+    if (ok) {
+      const float l = LSE[int64_t(bh) * N + qrow];
+      lse2 = l == kNegInf ? kInfB : l * kLog2e;  // a row that sees no key gets P = 0
+      dl = DELTA[int64_t(bh) * N + qrow];
+    }
+  }
+  f32x16_t acc[G::NDB];
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16_t{};
+
+  // Staging: chunk i of a thread is row (tid + 256 i) / CPR, column (tid + 256 i) % CPR
+  // of the 64-key tile; rows past the end read the last row (finite; masked below).
+  u32x4_t sk[G::SPT], sv[G::SPT];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < G::SPT; ++i) {
+      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
+      const int64_t gr = min(t * kTile + r, N - 1);
+      sk[i] = load16(Kh + gr * D + col * 8);
+      sv[i] = load16(Vh + gr * D + col * 8);
+    }
+  };
+  auto lstore = [&](int slot) {
+    uint8_t* s = smem + slot * SLOT;
+#pragma unroll
+    for (int i = 0; i < G::SPT; ++i) {
+      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
+      *reinterpret_cast<u32x4_t*>(s + r * G::RS + col * 16) = sk[i];
+      *reinterpret_cast<u32x4_t*>(s + G::RT + r * G::CS + col * 16) = sk[i];
+      *reinterpret_cast<u32x4_t*>(s + G::RT + G::CT + r * G::RS + col * 16) = sv[i];
+    }
+  };
+  const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
+  const int first_masked = CAUSAL ? min(N >> 5, qw0 >> 5) : (N >> 5);
+
+  auto step = [&](int g, const uint8_t* s) {
+    const int b = (g & 1) * 32;
+    const uint8_t* kr = s + b * G::RS + roff;
+    const uint8_t* kt = s + G::RT + b * G::CS + toff;
+    const uint8_t* vr = s + G::RT + G::CT + b * G::RS + roff;
+    f32x16_t st = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int c2 = 0; c2 < G::NCH; ++c2) {
+      st = mfma(frag_row(kr, c2), as_bf16x8(qf[c2]), st);
+      dp = mfma(frag_row(vr, c2), as_bf16x8(df[c2]), dp);
+    }
+    if (g >= first_masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * g + swap23(8 * (r >> 2) + 4 * half + (r & 3));
+        if (key >= N || (CAUSAL && key > qrow)) st[r] = kNegInf;
+      }
+    }
+    uint32_t ds[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = exp2_hw(fmaf(st[2 * i], c, -lse2));
+      const float p1 = exp2_hw(fmaf(st[2 * i + 1], c, -lse2));
+      ds[i] = pack_bf16x2(p0 * (dp[2 * i] - dl), p1 * (dp[2 * i + 1] - dl));
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const u32x4_t bop = {ds[4 * cc], ds[4 * cc + 1], ds[4 * cc + 2], ds[4 * cc + 3]};
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db)
+        acc[db] = mfma(frag_tr(kt, cc, db, G::CS), as_bf16x8(bop), acc[db]);
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 1 < ntiles) gload(t + 1);
+    const uint8_t* s = smem + (t & 1) * SLOT;
+    if (2 * t < nblk) step(2 * t, s);
+    if (2 * t + 1 < nblk) step(2 * t + 1, s);
+    if (t + 1 < ntiles) lstore((t + 1) & 1);  // slot read during tile t-1, before its barrier
+    __syncthreads();
+  }
+
+  if (qrow < N) {
+    float* orow = dQ + head + int64_t(qrow) * D;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4_t val = {acc[db][4 * g4] * scale, acc[db][4 * g4 + 1] * scale,
+                             acc[db][4 * g4 + 2] * scale, acc[db][4 * g4 + 3] * scale};
+        *reinterpret_cast<f32x4_t*>(orow + 32 * db + 8 * g4 + 4 * half) = val;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ dK,
+    float* __restrict__ dV, int N, int BH, int nkt, float c, float scale) {
+  using G = BGeo<D>;
+  // Q rows, Q transposing copy, dO rows, dO transposing copy, then lse2 and Delta of
+  // the tile's 64 queries.
+  constexpr int SLOT = 2 * G::RT + 2 * G::CT + 2 * kTile * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  int bh, kt;
+  map_bwd(blockIdx.x, BH, nkt, CAUSAL, false, bh, kt);
+  const int64_t head = int64_t(bh) * N * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* dOh = dO + head;
+  const float* lseh = LSE + int64_t(bh) * N;
+  const float* delh = DELTA + int64_t(bh) * N;
+  const int k0 = kt * kRowsB, kw0 = k0 + 32 * wave, krow = kw0 + l32;
+
+  // Query blocks this wavefront folds: [gs, nblk_all) (causal: from its diagonal).
+  const int nblk_all = (N + 31) >> 5;
+  const int gs = kw0 >= N ? nblk_all : (CAUSAL ? (kw0 >> 5) : 0);
+  const int t_first = CAUSAL ? (k0 >> 6) : 0;          // first tile the workgroup stages
+  const int ntiles_all = (nblk_all + 1) >> 1;
+
+  // Own rows: K^T and V^T as B operands (k = head dims 16 c2 + 8 half + 0..7).
+  u32x4_t kf[G::NCH], vf[G::NCH];
+  {
+    const bool ok = krow < N;
+#pragma unroll
+    for (int c2 = 0; c2 < G::NCH; ++c2) {
+      kf[c2] = ok ? load16(K + head + int64_t(krow) * D + 16 * c2 + 8 * half) : u32x4_t{0, 0, 0, 0};
+      vf[c2] = ok ? load16(V + head + int64_t(krow) * D + 16 * c2 + 8 * half) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+  f32x16_t dva[G::NDB], dka[G::NDB];
+#pragma unroll
+  for (int db = 0; db < G::NDB; ++db) {
+    dva[db] = f32x16_t{};
+    dka[db] = f32x16_t{};
+  }
+
+  u32x4_t sq[G::SPT], sd[G::SPT];
+  float sl = 0.f, sdl = 0.f;
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < G::SPT; ++i) {
+      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
+      const int64_t gr = min(t * kTile + r, N - 1);
+      sq[i] = load16(Qh + gr * D + col * 8);
+      sd[i] = load16(dOh + gr * D + col * 8);
+    }
+    if (tid < kTile) {
+      const int q = t * kTile + tid;
+      const float l = q < N ? lseh[q] : kNegInf;
+      sl = l == kNegInf ? kInfB : l * kLog2e;  // padding or key-less rows: P = 0
+      sdl = q < N ? delh[q] : 0.f;
+    }
+  };
+  auto lstore = [&](int slot) {
+    uint8_t* s = smem + slot * SLOT;
+#pragma unroll
+    for (int i = 0; i < G::SPT; ++i) {
+      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
+      *reinterpret_cast<u32x4_t*>(s + r * G::RS + col * 16) = sq[i];
+      *reinterpret_cast<u32x4_t*>(s + G::RT + r * G::CS + col * 16) = sq[i];
+      *reinterpret_cast<u32x4_t*>(s + G::RT + G::CT + r * G::RS + col * 16) = sd[i];
+      *reinterpret_cast<u32x4_t*>(s + 2 * G::RT + G::CT + r * G::CS + col * 16) = sd[i];
+    }
+    if (tid < kTile) {
+      float* f = reinterpret_cast<float*>(s + 2 * G::RT + 2 * G::CT);
+      f[tid] = sl;
+      f[kTile + tid] = sdl;
+    }
+  };
+  const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
+
+  auto step = [&](int g, const uint8_t* s) {
+    const int b = (g & 1) * 32;
+    const uint8_t* qr = s + b * G::RS + roff;
+    const uint8_t* qt = s + G::RT + b * G::CS + toff;
+    const uint8_t* dr = s + G::RT + G::CT + b * G::RS + roff;
+    const uint8_t* dt = s + 2 * G::RT + G::CT + b * G::CS + toff;
+    const float* fl = reinterpret_cast<const float*>(s + 2 * G::RT + 2 * G::CT) + b;
+    f32x16_t st = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int c2 = 0; c2 < G::NCH; ++c2) {
+      st = mfma(frag_row(qr, c2), as_bf16x8(kf[c2]), st);
+      dp = mfma(frag_row(dr, c2), as_bf16x8(vf[c2]), dp);
+    }
+    // Registers 8 cc + i hold query 32 g + 16 cc + 8 half + i.
+    f32x4_t l2[4], d2[4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        l2[2 * cc + h4] = *reinterpret_cast<const f32x4_t*>(fl + 16 * cc + 8 * half + 4 * h4);
+        d2[2 * cc + h4] = *reinterpret_cast<const f32x4_t*>(fl + kTile + 16 * cc + 8 * half + 4 * h4);
+      }
+    const bool masked = (32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32);
+    uint32_t pk[8], dsk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float sv[2], pv[2], dv2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * i + e;             // register r = 8 cc + j
+        const int cc = r >> 3, j = r & 7;
+        const float lq = l2[2 * cc + (j >> 2)][j & 3], dq = d2[2 * cc + (j >> 2)][j & 3];
+        const int q = 32 * g + 16 * cc + 8 * half + j;
+        sv[e] = st[r];
+        if (masked && (q >= N || (CAUSAL && krow > q))) sv[e] = kNegInf;
+        pv[e] = exp2_hw(fmaf(sv[e], c, -lq));
+        dv2[e] = pv[e] * (dp[r] - dq);
+      }
+      pk[i] = pack_bf16x2(pv[0], pv[1]);
+      dsk[i] = pack_bf16x2(dv2[0], dv2[1]);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const u32x4_t bp = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
+      const u32x4_t bs = {dsk[4 * cc], dsk[4 * cc + 1], dsk[4 * cc + 2], dsk[4 * cc + 3]};
+#pragma unroll
+      for (int db = 0; db < G::NDB; ++db) {
+        dva[db] = mfma(frag_tr(dt, cc, db, G::CS), as_bf16x8(bp), dva[db]);
+        dka[db] = mfma(frag_tr(qt, cc, db, G::CS), as_bf16x8(bs), dka[db]);
+      }
+    }
+  };
+
+  const int ntiles = k0 >= N ? 0 : ntiles_all - t_first;
+  if (ntiles > 0) {
+    gload(t_first);
+    lstore(0);
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int i = 0; i < ntiles; ++i) {
+    const int t = t_first + i;
+    if (i + 1 < ntiles) gload(t + 1);
+    const uint8_t* s = smem + (i & 1) * SLOT;
+    if (2 * t >= gs && 2 * t < nblk_all) step(2 * t, s);
+    if (2 * t + 1 >= gs && 2 * t + 1 < nblk_all) step(2 * t + 1, s);
+    if (i + 1 < ntiles) lstore((i + 1) & 1);  // slot read during tile t-1, before its barrier
+    __syncthreads();
+  }
+
+  if (krow < N) {
+    float* vrow = dV + head + int64_t(krow) * D;
+    float* krw = dK + head + int64_t(krow) * D;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = 32 * db + 8 * g4 + 4 * half;
+        *reinterpret_cast<f32x4_t*>(vrow + col) =
+            f32x4_t{dva[db][4 * g4], dva[db][4 * g4 + 1], dva[db][4 * g4 + 2], dva[db][4 * g4 + 3]};
+        *reinterpret_cast<f32x4_t*>(krw + col) =
+            f32x4_t{dka[db][4 * g4] * scale, dka[db][4 * g4 + 1] * scale,
+                    dka[db][4 * g4 + 2] * scale, dka[db][4 * g4 + 3] * scale};
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdArgs& a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const int64_t rows = int64_t(BH) * a.N;
+  const float c = a.scale * kLog2e;
+  const auto* q = static_cast<const uint16_t*>(a.q);
+  const auto* k = static_cast<const uint16_t*>(a.k);
+  const auto* v = static_cast<const uint16_t*>(a.v);
+  const auto* dout = static_cast<const uint16_t*>(a.dout);
+  const int64_t dblocks = (rows + 15) / 16;
+  const int nt = (a.N + kRowsB - 1) / kRowsB;
+  const int64_t blocks = int64_t(BH) * nt;
+  if (dblocks > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((delta_kernel<D>), dim3(unsigned(dblocks)), dim3(256), 0, s, dout, a.o,
+                     a.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreadsB), 0, s, q, k,
+                     v, dout, a.lse, a.delta, a.dq, a.N, BH, nt, c, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreadsB), 0, s, q,
+                     k, v, dout, a.lse, a.delta, a.dk, a.dv, a.N, BH, nt, c, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
+  if (a.D == 128) return a.causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+  return a.causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
+}
+
+}  // namespace fa

@@ -17,6 +17,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kInfB = __builtin_inff();
 
 // 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }

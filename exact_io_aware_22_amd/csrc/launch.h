@@ -39,10 +39,28 @@ struct CombineArgs {
   int rows, splits, D;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* o;
+  const float* lse;
+  const void* dout;
+  float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int B, H, N, D;
+  float scale;
+  bool causal;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode_partials_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_partials_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine_partials(const CombineArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

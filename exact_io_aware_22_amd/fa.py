@@ -23,8 +23,8 @@ _lib = None
 
 FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
-EXPORTED = ("fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_strerror",
-            "fa_abi_version")
+EXPORTED = ("fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_backward",
+            "fa_strerror", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -48,6 +48,8 @@ def load():
     lib.fa_decode_partials.restype = i
     lib.fa_combine_partials.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
     lib.fa_combine_partials.restype = i
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_backward.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -116,6 +118,21 @@ def fa_combine_partials(m, d, o_part, o, lse, stream=None) -> None:
     _check(code, "fa_combine_partials")
 
 
+def fa_backward(q, k, v, o, lse, dout, delta, dq, dk, dv, scale: float, causal: bool,
+                stream=None) -> None:
+    """q, k, v, dout: [B, H, N, D] (bf16 or fp32, same dtype); o: [B, H, N, D] fp32 and
+    lse: [B, H, N] fp32 from fa_forward; delta: [B, H, N] fp32 scratch; dq, dk, dv:
+    [B, H, N, D] fp32, written."""
+    _dense(q, k, v, o, lse, dout, delta, dq, dk, dv)
+    B, H, N, D = q.shape
+    if dout.dtype != q.dtype:
+        raise TypeError("dout must have the dtype of q, k and v")
+    code = load().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                              _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, D,
+                              float(scale), int(bool(causal)), _dtype_code(q), _stream(stream))
+    _check(code, "fa_backward")
+
+
 # ------------------------------------------------------------------ conveniences
 def forward(q, k, v, scale: float | None = None, causal: bool = False, stream=None):
     """Allocate O [B, H, N, D] fp32 and lse [B, H, N] fp32 and run fa_forward."""
@@ -126,6 +143,20 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, stream=No
     lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     fa_forward(q, k, v, o, lse, scale, causal, stream)
     return o, lse
+
+
+def backward(q, k, v, o, lse, dout, scale: float | None = None, causal: bool = False,
+             stream=None):
+    """Allocate Delta scratch and dq, dk, dv [B, H, N, D] fp32 and run fa_backward.
+    o and lse are the outputs of `forward` for the same q, k, v, scale and causal."""
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    delta = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(B, H, N, D, dtype=torch.float32, device=dev) for _ in range(3))
+    fa_backward(q, k, v, o, lse, dout, delta, dq, dk, dv, scale, causal, stream)
+    return dq, dk, dv
 
 
 def decode(q, k, v, splits: int, scale: float | None = None, stream=None, return_partials=False):

@@ -1,6 +1,6 @@
 /*
- * fa.h -- C ABI of libfa.so: exact tiled attention forward and split-KV decode
- * for AMD Instinct MI355X (gfx950).
+ * fa.h -- C ABI of libfa.so: exact tiled attention forward, its backward, and
+ * split-KV decode for AMD Instinct MI355X (gfx950).
  *
  * What is computed (definitions from "Learning FlashAttention the Hard Way --
  * Part 1", cloudrift.ai):
@@ -48,8 +48,8 @@ enum {
   FA_ERR_SHAPE = -2, /* negative size, D not in {64, 128}, splits < 1, or a size
                         whose element count does not fit in 63 bits                 */
   FA_ERR_DTYPE = -3, /* dtype is neither FA_F32 nor FA_BF16                         */
-  FA_ERR_ALIGN = -4, /* q, k, v, o or o_part is not 16-byte aligned; m, d, lse not
-                        4-byte aligned                                              */
+  FA_ERR_ALIGN = -4, /* a tensor pointer is not 16-byte aligned; m, d, lse or delta
+                        not 4-byte aligned                                          */
   FA_ERR_ARG = -5,   /* scale not finite or not > 0, or causal not 0 or 1           */
   FA_ERR_HIP = -6    /* the HIP runtime rejected the kernel launch                   */
 };
@@ -107,6 +107,31 @@ int fa_decode_partials(const void* q, const void* k, const void* v, float* m, fl
  */
 int fa_combine_partials(const float* m, const float* d, const float* o_part, int splits,
                         int rows, int D, float* o, float* lse, void* stream);
+
+/*
+ * fa_backward -- gradients of the attention forward with respect to q, k and v.
+ * The pages name the backward pass that recomputes the attention matrix from the
+ * per-row log-sum-exp instead of storing it, without printing formulas; the
+ * gradients follow from the forward definition by the chain rule (dV = P^T dO,
+ * dP = dO V^T, dS = P (dP - Delta) with Delta_i = sum_d dO_id O_id, dQ = scale dS K,
+ * dK = scale dS^T Q), with P recomputed from lse.
+ *
+ *   q, k, v : [B][H][N][D] of `dtype`, the forward's inputs.
+ *   o       : [B][H][N][D] float32 and
+ *   lse     : [B][H][N] float32, the outputs fa_forward wrote for the same inputs,
+ *             scale and causal (read only).
+ *   dout    : [B][H][N][D] of `dtype`, the gradient of the loss with respect to o.
+ *   delta   : [B][H][N] float32 caller-owned scratch, written (Delta_i); its
+ *             contents on return are defined (Delta) but not part of the result.
+ *   dq, dk, dv : [B][H][N][D] float32, written (overwritten, not accumulated).
+ *   scale, causal, D : as for fa_forward.
+ * For bfloat16 the products take bfloat16 operands (P and dS are rounded to
+ * bfloat16 before the products that consume them) and accumulate in float32.
+ * Alignment: q, k, v, o, dout, dq, dk, dv 16 bytes; lse, delta 4 bytes.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* delta, float* dq, float* dk, float* dv, int B, int H,
+                int N, int D, float scale, int causal, int dtype, void* stream);
 
 /* Static, human-readable name of an FA_* code (never NULL). */
 const char* fa_strerror(int code);

@@ -35,7 +35,8 @@ def lib():
 
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_strerror", "fa_abi_version"])
+        ["fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_backward", "fa_strerror",
+         "fa_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -117,6 +118,29 @@ def test_combine_validation(lib):
     assert comb(lib, lse=P + 1) == ALIGN
     assert comb(lib, rows=0) == OK
     assert comb(lib, rows=0, m=None, o=None) == OK
+
+
+def bwd(lib, q=P, k=P, v=P, o=P, lse=P, do=P, delta=P, dq=P, dk=P, dv=P, B=1, H=2, N=8, D=128,
+        scale=0.1, causal=1, dtype=1):
+    return lib.fa_backward(q, k, v, o, lse, do, delta, dq, dk, dv, B, H, N, D, scale, causal,
+                           dtype, None)
+
+
+def test_backward_validation(lib):
+    for name in ("q", "k", "v", "o", "lse", "do", "delta", "dq", "dk", "dv"):
+        assert bwd(lib, **{name: None}) == NULL, name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert bwd(lib, **{name: P + 8}) == ALIGN, name
+    assert bwd(lib, lse=P + 2) == ALIGN
+    assert bwd(lib, delta=P + 1) == ALIGN
+    assert bwd(lib, N=-1) == SHAPE
+    assert bwd(lib, D=48) == SHAPE
+    assert bwd(lib, dtype=2) == DTYPE
+    assert bwd(lib, scale=0.0) == ARG
+    assert bwd(lib, causal=-1) == ARG
+    assert bwd(lib, B=0) == OK
+    assert bwd(lib, N=0, q=None, dq=None, delta=None) == OK
+    assert bwd(lib, N=0, D=40) == SHAPE
 
 
 def test_binding_raises_with_message(lib):
