@@ -4,7 +4,8 @@
 Prints ONE JSON line. A step is one fa_forward over the headline workload
 (bf16, B=2, H=32, N=8192, D=128, causal, q and k ~ N(0, 9)); `value` is its
 throughput in TFLOP/s under the 4*B*H*N^2*D (halved for causal) convention.
-The same line carries the split-KV decode (bf16, B=16, H=32, one query row, 32768
+The same line carries the backward pass on the headline inputs (TFLOP/s, 2.5x-forward
+convention), the split-KV decode (bf16, B=16, H=32, one query row, 32768
 keys, D=128, 64 chunks of 512) as HBM GB/s, the other prefill workloads' rates,
 a live roofline of the dominant kernel, a sampled parity check of the timed
 outputs against the fp64 oracle, and the oracle itself timed on the host cores.
@@ -226,6 +227,48 @@ def cpu_baseline(q, k, v, w, budget_s: float):
             "seconds": t_used, "cpu_model": cpu}
 
 
+def bench_backward(steps: int, warmup: int, torch, fa, make_inputs, W, check: bool):
+    """fa_backward (Delta, dQ, dK/dV kernels) on the headline workload's inputs with a
+    seeded upstream gradient; flops under the usual 2.5x-forward convention (five
+    products: S recomputed, dV, dP, dQ, dK), halved for causal."""
+    import numpy as np
+
+    from exact_io_aware_22_amd.workloads import random_tensor
+
+    w = W[HEADLINE]
+    q, k, v = make_inputs(w)
+    do = random_tensor(tuple(q.shape), 99, torch.bfloat16)
+    qd, kd, vd, dd = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fa.forward(qd, kd, vd, w.scale, w.causal)
+    delta = torch.empty(w.B, w.H, w.N, device="cuda")
+    dq, dk, dv = (torch.empty(w.B, w.H, w.N, w.D, device="cuda") for _ in range(3))
+    ms = time_launches(lambda: fa.fa_backward(qd, kd, vd, o, lse, dd, delta, dq, dk, dv, w.scale,
+                                              w.causal), steps, warmup, torch)
+    flops = 2.5 * w.flops()
+    achieved = flops / (ms * 1e-3) / 1e12
+    res = {"workload": HEADLINE, "ms_per_step": ms, "value": achieved, "unit": "TFLOP/s",
+           "flop_convention": "2.5 x forward (5 products), halved for causal",
+           "roofline": {"kernels": "delta_kernel + dq_kernel + dkdv_kernel", "bound": "mfma",
+                        "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                        "algorithmic_flops_per_launch": flops}}
+    if check:
+        import oracle
+
+        b, h = w.B - 1, w.H - 1
+        ref = oracle.attention_backward(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1],
+                                        v[b:b + 1, h:h + 1], do[b:b + 1, h:h + 1], w.scale,
+                                        w.causal)[:3]
+        errs = {}
+        for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            gg = g[b:b + 1, h:h + 1].cpu().double().numpy()
+            errs[name] = float(np.max(np.abs(gg - r)) / max(1.0, np.max(np.abs(r))))
+        res["parity"] = {"head": [b, h], "normwise_err": errs, "tol": 1e-2}
+    del qd, kd, vd, dd, o, lse, delta, dq, dk, dv
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(torch, nbytes: int, steps: int):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -241,7 +284,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "copy"],
+                    default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -304,6 +348,10 @@ def main() -> int:
                 r["frac_of_bf16_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
                 out["also"].append(r)
                 torch.cuda.empty_cache()
+    if args.only in ("all", "backward"):
+        log(f"timing the backward on {HEADLINE}")
+        out["backward"] = bench_backward(max(3, args.steps // 5), max(2, args.warmup // 10), torch,
+                                         fa, make_inputs, WORKLOADS, check=args.only == "all")
     if args.only in ("all", "decode"):
         log(f"timing {DECODE}")
         out["decode"] = bench_decode(args.steps, args.warmup, torch, fa, make_inputs, WORKLOADS)
