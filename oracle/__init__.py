@@ -17,3 +17,4 @@ from .fp64 import (  # noqa: F401
     split_bounds,
 )
 from .backward import attention_backward  # noqa: F401,E402
+from .masks import attention_varlen, attention_window, visible  # noqa: F401,E402
