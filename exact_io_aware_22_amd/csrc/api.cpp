@@ -38,27 +38,47 @@ const char* fa_strerror(int code) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape: negative size, D not 64 or 128, splits < 1, or too large";
-    case FA_ERR_DTYPE: return "unsupported dtype (expected FA_F32 or FA_BF16)";
+    case FA_ERR_DTYPE: return "unsupported dtype (FA_F32 or FA_BF16; windows and packed sequences need FA_BF16)";
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, m/d/lse/delta 4-byte alignment)";
-    case FA_ERR_ARG: return "invalid argument: scale must be finite and > 0, causal 0 or 1";
+    case FA_ERR_ARG: return "invalid argument: scale must be finite and > 0, causal 0 or 1, windows >= -1";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     default: return "unknown fa error code";
   }
 }
 
-int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B,
-               int H, int N, int D, float scale, int causal, int dtype, void* stream) {
-  if (B < 0 || H < 0 || N < 0 || !head_dim_ok(D) || !count_ok(B, H, N, D)) return FA_ERR_SHAPE;
+int fa_forward_ext(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                   int H, int N, int D, float scale, int causal, int window_left,
+                   int window_right, const int* cu_seqlens, int max_seqlen, int dtype,
+                   void* stream) {
+  const bool packed = cu_seqlens != nullptr;
+  // Packed tensors are [H][N][D]: size-check H x N x D (B counts sequences).
+  if (B < 0 || H < 0 || N < 0 || !head_dim_ok(D) ||
+      !count_ok(packed ? 1 : B, H, N, D) || (packed && max_seqlen < 0))
+    return FA_ERR_SHAPE;
   if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (!std::isfinite(scale) || !(scale > 0.0f) || (causal != 0 && causal != 1)) return FA_ERR_ARG;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;  // empty: no pointer is touched
+  if (!std::isfinite(scale) || !(scale > 0.0f) || (causal != 0 && causal != 1) ||
+      window_left < -1 || window_right < -1)
+    return FA_ERR_ARG;
+  const bool windowed = window_left >= 0 || window_right >= 0;
+  if (dtype == FA_F32 && (windowed || packed)) return FA_ERR_DTYPE;  // bf16 kernels only
+  if (B == 0 || H == 0 || N == 0 || (packed && max_seqlen == 0)) return FA_OK;  // empty
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(lse, 4))
+      !aligned(lse, 4) || !aligned(cu_seqlens, 4))
     return FA_ERR_ALIGN;
   fa::FwdArgs a{q, k, v, o, lse, B, H, N, D, scale, causal == 1};
+  a.window_left = window_left;
+  a.window_right = window_right;
+  a.cu_seqlens = cu_seqlens;
+  a.max_seqlen = max_seqlen;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+               int H, int N, int D, float scale, int causal, int dtype, void* stream) {
+  return fa_forward_ext(q, k, v, o, lse, B, H, N, D, scale, causal, -1, -1, nullptr, 0, dtype,
+                        stream);
 }
 
 int fa_decode_partials(const void* q, const void* k, const void* v, float* m, float* d,

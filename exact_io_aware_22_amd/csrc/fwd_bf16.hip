@@ -105,11 +105,17 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nqt, bool causal, 
   if (causal) qt = nqt - 1 - qt;
 }
 
+// Dense: units are the B*H heads of [B][H][Ntot][D] tensors. Packed (cu != nullptr):
+// units are (head, sequence) pairs of [H][Ntot][D] tensors, sequence s owning rows
+// [cu[s], cu[s+1]) (values clamped into [0, Ntot], length capped at max_len).
+// Window: key j visible to query i iff i - wl <= j <= i + wr (negative = unbounded);
+// causal is the wr = 0 case.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int N,
-    int BH, int nqt, float c) {
+    const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE, int Ntot,
+    int U, int nqt, float c, int wl, int wr_in, const int* __restrict__ cu, int nseq,
+    int max_len) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[G::LDS];
   uint8_t* const kring = smem;
@@ -118,20 +124,48 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int half = lane >> 5, l32 = lane & 31;
-  int bh, qt;
-  map_tile(blockIdx.x, BH, nqt, CAUSAL, bh, qt);
+  int unit, qt;
+  map_tile(blockIdx.x, U, nqt, CAUSAL, unit, qt);
+  int N;            // rows of this unit
+  int64_t row0;     // its first row within the [.][Ntot] row space
+  if (cu != nullptr) {
+    const int h = unit / nseq, sq = unit % nseq;
+    const int a = min(max(cu[sq], 0), Ntot), b = min(max(cu[sq + 1], a), Ntot);
+    N = min(b - a, max_len);
+    row0 = int64_t(h) * Ntot + a;
+  } else {
+    N = Ntot;
+    row0 = int64_t(unit) * Ntot;
+  }
+  // Uniform by construction; readfirstlane lets the compiler keep them in SGPRs.
+  N = __builtin_amdgcn_readfirstlane(N);
+  row0 = int64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(row0))))) |
+         (int64_t(__builtin_amdgcn_readfirstlane(int(row0 >> 32))) << 32);
   const int q0 = qt * kBM;
-  const int64_t head = int64_t(bh) * N * D;
+  if (q0 >= N) return;  // the whole workgroup leaves before any barrier
+  const int64_t head = row0 * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
+  const int wr = CAUSAL ? 0 : wr_in;  // causal bounds the window on the right at 0
 
-  // Blocks of 32 keys: this wavefront folds blocks [0, nblk); the workgroup stages
-  // tiles [0, ntiles) covering the most any of its wavefronts needs.
+  // Blocks of 32 keys: this wavefront folds blocks [g_lo, nblk) (the window's edges,
+  // causal diagonal and N); the workgroup stages tiles [t_lo, ntiles) covering them.
   const int qw0 = q0 + 32 * wave;  // first query row of this wavefront
   const int nblk_all = (N + 31) >> 5;
-  const int nblk = qw0 >= N ? 0 : (CAUSAL ? min(nblk_all, (qw0 >> 5) + 1) : nblk_all);
-  const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kBM) - 1) >> 5) + 1) : nblk_all;
+  // One past the last block a query qlast <= N - 1 may see (wr is capped at the distance
+  // to the last key before it is added, so no sum overflows).
+  auto end_blk = [&](int qlast) {
+    return wr < 0 ? nblk_all : min(nblk_all, ((qlast + min(wr, N - 1 - qlast)) >> 5) + 1);
+  };
+  // g_lo is rounded down to an even block, so a wavefront's first block always opens
+  // a tile and its scores always land in the same register set; the block added that
+  // way lies wholly left of the window and is folded in fully masked, i.e. as the
+  // identity.
+  const int g_lo = (qw0 >= N || wl < 0) ? 0 : ((max(0, qw0 - wl) >> 5) & ~1);
+  const int nblk = qw0 >= N ? 0 : end_blk(qw0 + 31);
+  const int nblk_wg = end_blk(min(N, q0 + kBM) - 1);
+  const int t_lo = wl < 0 ? 0 : (max(0, q0 - wl) >> 6);
   const int ntiles = (nblk_wg + 1) >> 1;
 
   // ---- staging by direct global -> LDS loads (global_load_lds_dwordx4): one such
@@ -149,20 +183,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   constexpr int CK = G::KSTRIDE / 16, CV = G::VSTRIDE / 16;  // chunks per padded row
   constexpr int MAXI = (CV + kWaves - 1) / kWaves;            // loads per wave per tile
   static_assert(CK <= CV && G::KTILE == CK * 1024 && G::VTILE == CV * 1024, "tile = C KB");
-  auto chunk_off = [&](int j, int C, int t, bool full) -> uint32_t {
+  // Source offset (bytes from the tile base) of lane's chunk of kilobyte j in a full tile.
+  auto chunk_off = [&](int j, int C) -> uint32_t __attribute__((always_inline)) {
     const int p = 64 * j + lane, r = p / C, col = min(p % C, G::CPR - 1);
-    const int row = full ? r : min(t * kBN + r, N - 1) - t * kBN;
-    return uint32_t(row * D * 2 + col * 16);
+    return uint32_t(r * D * 2 + col * 16);
   };
   uint32_t dk[MAXI], dv[MAXI];
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
-    dk[i] = chunk_off(wave + kWaves * i, CK, 0, true);
-    dv[i] = chunk_off(wave + kWaves * i, CV, 0, true);
+    dk[i] = chunk_off(wave + kWaves * i, CK);
+    dv[i] = chunk_off(wave + kWaves * i, CV);
   }
+  // The same chunk in tile t when rows past N - 1 are redirected to row N - 1 (its row
+  // is off / (2D), a power-of-two division).
+  auto clamp_off = [&](uint32_t off, int t) -> uint32_t __attribute__((always_inline)) {
+    constexpr int kRowShift = __builtin_ctz(2 * D);
+    const int r = int(off >> kRowShift);
+    return off - uint32_t((r - (min(t * kBN + r, N - 1) - t * kBN)) << kRowShift);
+  };
   auto dma = [&](const uint16_t* src, uint8_t* slot, int C, const uint32_t (&d)[MAXI], int t,
-                 bool full) {
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(src) + int64_t(t) * kBN * D * 2;
+                 bool full) __attribute__((always_inline)) {
+    // The tile base is uniform; readfirstlane keeps it in the SGPR pair the load takes.
+    const uint64_t b64 = reinterpret_cast<uint64_t>(src) + uint64_t(t) * kBN * D * 2;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(
+        uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64))))) |
+        (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
     const bool ragged = !full && t * kBN + kBN > N;
     const uint32_t lds0 =
         uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(uint8_t, slot)));
@@ -170,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     for (int i = 0; i < MAXI; ++i) {
       const int j = wave + kWaves * i;
       if (j < C) {
-        const uint32_t off = ragged ? chunk_off(j, C, t, false) : d[i];
+        const uint32_t off = ragged ? clamp_off(d[i], t) : d[i];
         const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
         asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :
@@ -209,12 +254,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // Fragments of S^T block g (32 keys x this wavefront's 32 queries): the K operand
   // rows from the K ring, one 16-byte read per 16-wide chunk of the head dim.
   // koff_blk / voff_blk: byte offset of a 32-key block in its ring (uniform).
-  auto kload = [&](int koff_blk, u32x4_t (&kf)[G::NCH]) {
+  auto kload = [&](int koff_blk, u32x4_t (&kf)[G::NCH]) __attribute__((always_inline)) {
     const uint8_t* kb = kring + koff_blk + koff;
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) kf[c2] = load16(kb + 32 * c2);
   };
-  auto qk = [&](const u32x4_t (&kf)[G::NCH]) {
+  auto qk = [&](const u32x4_t (&kf)[G::NCH]) __attribute__((always_inline)) {
     f32x16_t s = f32x16_t{};
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2)
@@ -223,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   };
   // O^T += V^T (block g) P^T (block g). A operand rows: head dims 32db + l32; k:
   // keys 16cc + 8*half + 0..7 of the block, from two transposing reads.
-  auto vload = [&](int voff_blk, u32x4_t (&vf)[2 * G::NDB]) {
+  auto vload = [&](int voff_blk, u32x4_t (&vf)[2 * G::NDB]) __attribute__((always_inline)) {
     const uint8_t* vb = vring + voff_blk + voff;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
@@ -237,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         vf[cc * G::NDB + db] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
       }
   };
-  auto pv = [&](const u32x4_t (&vf)[2 * G::NDB], const uint32_t (&pk)[8]) {
+  auto pv = [&](const u32x4_t (&vf)[2 * G::NDB], const uint32_t (&pk)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const u32x4_t b = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
@@ -247,19 +292,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
                                                            as_bf16x8(b), oacc[db], 0, 0, 0);
     }
   };
-  auto apply_mask = [&](int g, f32x16_t& s) {
-    const int qi = qw0 + l32;
+  // Masks block g: key 32g + k is visible to query qw0 + l32 iff the key is below N
+  // and rel = key - query lies in [rlo, rhi] (an unbounded side: the int range).
+  const int rlo = wl < 0 ? INT_MIN : -wl, rhi = wr < 0 ? INT_MAX : wr;
+  auto apply_mask = [&](int g, f32x16_t& s) __attribute__((always_inline)) {
+    const int rel0 = 32 * g - (qw0 + l32);
+    const int lim = N - 32 * g;  // key 32g + k exists iff k < lim
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 32 * g + swap23(8 * (r >> 2) + 4 * half + (r & 3));
-      if (key >= N || (CAUSAL && key > qi)) s[r] = kNegInf;
+      const int k = swap23(8 * (r >> 2) + 4 * half + (r & 3));
+      const int rel = rel0 + k;
+      if (k >= lim || rel > rhi || rel < rlo) s[r] = kNegInf;
     }
   };
   // Softmax of block g against the reference maximum; returns the factor the
   // accumulator must be multiplied by before block g is added (1 if unchanged).
   // Weights of one block against the reference, packed to bf16 for the PV MFMA, with
   // their float32 sum (ps) and the sum of the packed values (pq).
-  auto weights = [&](const f32x16_t& s, float nmc, uint32_t (&pk)[8], float& ps, float& pq) {
+  auto weights = [&](const f32x16_t& s, float nmc, uint32_t (&pk)[8], float& ps, float& pq) __attribute__((always_inline)) {
     const bf16x2_t ones = as_bf16x2(0x3f803f80u);
     ps = 0.f;
     pq = 0.f;
@@ -277,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // block, whose reference is -inf) does the wavefront take the rare path: the
   // block's maximum becomes the reference, O owes the factor alpha, and the block is
   // weighted again. No weight above 2^kTau is ever kept.
-  auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8]) {
+  auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8]) __attribute__((always_inline)) {
     float ps, pq, alpha = 1.f;
     weights(s, nmc_ref, pk, ps, pq);
     if (__builtin_amdgcn_ballot_w64(!(ps <= kSumLimit))) {
@@ -297,20 +347,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     d_out = fmaf(d_out, alpha, pq);
     return alpha;
   };
-  auto rescale = [&](float alpha) {
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) oacc[db] *= alpha;
     }
   };
-  // Blocks from first_masked on need masking: the ragged tail (32g + 32 > N) and,
-  // causal, keys past this wavefront's first query (32g + 31 > qw0, qw0 a multiple of 32).
-  const int first_masked = CAUSAL ? min(N >> 5, qw0 >> 5) : (N >> 5);
+  // Blocks from first_masked on need masking: the ragged tail (32g + 32 > N) and keys
+  // past the window's right edge for this wavefront's first query (qw0 + wr, qw0 a
+  // multiple of 32; the causal diagonal when wr = 0). Blocks up to mask_lo_end need it
+  // for the window's left edge of its last query.
+  const int first_masked = wr < 0 ? (N >> 5) : min(N >> 5, (qw0 + min(wr, N) + 1) >> 5);
+  const int mask_lo_end = wl < 0 ? -1 : ((qw0 + 31 - wl) >> 5);
 
-  // ---- prologue: K tiles 0 and 1 and V tile 0 in slots 0, 1, 0; V tile 1 loaded.
-  dma(Kh, kring, CK, dk, 0, false);
-  dma(Vh, vring, CV, dv, 0, false);
-  if (ntiles > 1) dma(Kh, kring + G::KTILE, CK, dk, 1, false);
+  // ---- prologue: K tiles t_lo and t_lo + 1 and V tile t_lo in slots 0, 1, 0.
+  dma(Kh, kring, CK, dk, t_lo, false);
+  dma(Vh, vring, CV, dv, t_lo, false);
+  if (t_lo + 1 < ntiles) dma(Kh, kring + G::KTILE, CK, dk, t_lo + 1, false);
   dma_wait();
   __syncthreads();
 
@@ -321,20 +374,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   uint32_t pa[8] = {0, 0, 0, 0, 0, 0, 0, 0}, pb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;  // factor O owes the reference of the latest softmax
   u32x4_t kf[G::NCH], vf[2 * G::NDB];
-  if (nblk > 0) {
-    kload(0, kf);
-    sa = qk(kf);
-  }
 
   // Step g: scores of block g in s_in, weights of block g-1 in p_in; K block g+1 at
   // kblk, V block g-1 at vblk. One basic block issues QK of block g+1 (issued even
   // past a wavefront's last block, reading a resident slot, result unused), PV of
-  // block g-1 (at g = 0 with zero weights against block 0) and the softmax of block
-  // g. The only branches come first: the mask of the diagonal / ragged block and the
-  // rare rescale of O.
+  // block g-1 (at a wavefront's first block g_lo with zero weights against block g_lo
+  // itself) and the softmax of block g. The only branches come first: the mask of the
+  // window-edge, diagonal or ragged blocks and the rare rescale of O.
   auto step = [&](int g, int kblk, int vblk, f32x16_t& s_in, f32x16_t& s_out,
-                  const uint32_t (&p_in)[8], uint32_t (&p_out)[8], bool unmasked) {
-    if (!unmasked && g >= first_masked) apply_mask(g, s_in);
+                  const uint32_t (&p_in)[8], uint32_t (&p_out)[8], bool unmasked) __attribute__((always_inline)) {
+    if (!unmasked && (g >= first_masked || g <= mask_lo_end)) apply_mask(g, s_in);
     // Bring O to the reference block g-1 was weighted against, then add PV(g-1).
     rescale(alpha_prev);
     kload(kblk, kf);
@@ -354,35 +403,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   int ks0 = 0, ks1 = G::KTILE, ks2 = 2 * G::KTILE;
   int vsp = 2 * G::VTILE, vs0 = 0, vs1 = G::VTILE;
   constexpr int KH = 32 * G::KSTRIDE, VH = 32 * G::VSTRIDE;  // second block of a tile
-  auto rotate = [&]() {
+  auto rotate = [&]() __attribute__((always_inline)) {
     const int k0 = ks0, v0 = vsp;
     ks0 = ks1; ks1 = ks2; ks2 = k0;
     vsp = vs0; vs0 = vs1; vs1 = v0;
   };
-  // Steady tiles [0, t_steady): both steps run unmasked, the wavefront's last block
-  // lies beyond the tile, and the tiles staged during it (t+1, t+2) are full, so the
-  // body needs no branch but the rescale. Every wavefront passes one barrier per tile
-  // in either loop, so the counts match across the workgroup.
-  const int last_free = min(first_masked, nblk - 1);  // blocks [0, last_free) plain
-  const int t_steady = max(0, min(min(last_free >> 1, ntiles - 2), (N >> 6) - 2));
-  int t = 0;
-#pragma unroll 1
-  for (; t < t_steady; ++t) {
-    dma(Kh, kring + ks2, CK, dk, t + 2, true);
-    dma(Vh, vring + vs1, CV, dv, t + 1, true);
-    step(2 * t, ks0 + KH, t > 0 ? vsp + VH : vs0, sa, sb, pa, pb, true);
-    step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, true);
-    dma_wait();
-    __syncthreads();
-    rotate();
-  }
-#pragma unroll 1
-  for (; t < ntiles; ++t) {
+  // Steady tiles [t_s0, t_s1): both steps run unmasked and past the wavefront's first
+  // block, its last block lies beyond the tile, and the tiles staged during it (t+1,
+  // t+2) are full, so the body needs no branch but the rescale. Other tiles take the
+  // general body. Every wavefront passes one barrier per tile of [t_lo, ntiles) in
+  // whichever loop, so the counts match across the workgroup.
+  const int last_free = min(first_masked, nblk - 1);  // blocks below it are plain
+  const int t_s0 = max(t_lo, (max(g_lo, mask_lo_end) + 2) >> 1);
+  const int t_s1 = max(t_s0, min(min(last_free >> 1, ntiles - 2), (N >> 6) - 2));
+  // Scores of a wavefront's first block g_lo (even, so it opens tile g_lo / 2), computed
+  // at the start of that tile, whose K is resident from its barrier on.
+  auto first_scores = [&]() __attribute__((always_inline)) {
+    kload(ks0, kf);
+    sa = qk(kf);
+  };
+  auto general_tile = [&](int t) __attribute__((always_inline)) {
     if (t + 2 < ntiles) dma(Kh, kring + ks2, CK, dk, t + 2, false);
     if (t + 1 < ntiles) dma(Vh, vring + vs1, CV, dv, t + 1, false);
-    if (2 * t < nblk) step(2 * t, ks0 + KH, t > 0 ? vsp + VH : vs0, sa, sb, pa, pb, false);
-    if (2 * t + 1 < nblk) step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, false);
-    if (nblk - 1 == 2 * t || nblk - 1 == 2 * t + 1) {
+    if (2 * t == g_lo && g_lo < nblk) first_scores();
+    // At g = g_lo the PV reads a resident V block with the zero weights of pb.
+    if (2 * t >= g_lo && 2 * t < nblk)
+      step(2 * t, ks0 + KH, 2 * t > g_lo ? vsp + VH : vs0, sa, sb, pa, pb, false);
+    if (2 * t >= g_lo && 2 * t + 1 < nblk) step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, false);
+    if (nblk - 1 >= g_lo && (nblk - 1 == 2 * t || nblk - 1 == 2 * t + 1)) {
       // This wavefront's last block is in tile t: fold it in while its V is resident.
       rescale(alpha_prev);
       vload(vs0 + ((nblk & 1) ? 0 : VH), vf);
@@ -391,6 +439,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     dma_wait();
     __syncthreads();
     rotate();
+  };
+  // One copy of each body: the general tile loop drops into the steady loop at t_s0.
+  // When the steady run is not empty it ends at t_s1 <= ntiles - 2, so a general tile
+  // follows it.
+#pragma unroll 1
+  for (int t = t_lo; t < ntiles; ++t) {
+    if (t == t_s0) {
+#pragma unroll 1
+      for (; t < t_s1; ++t) {
+        dma(Kh, kring + ks2, CK, dk, t + 2, true);
+        dma(Vh, vring + vs1, CV, dv, t + 1, true);
+        step(2 * t, ks0 + KH, vsp + VH, sa, sb, pa, pb, true);
+        step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, true);
+        dma_wait();
+        __syncthreads();
+        rotate();
+      }
+    }
+    general_tile(t);
   }
 
   // ---- read out: o / d once, lse = ln(sum) = (r c + log2 d) ln 2
@@ -408,20 +475,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         *reinterpret_cast<f32x4_t*>(orow + 32 * db + 8 * g4 + 4 * half) = val;
       }
     if (half == 0)
-      LSE[int64_t(bh) * N + qi] = dl > 0.f ? (m_ref * c + log2_hw(dl)) * kLn2 : kNegInf;
+      LSE[row0 + qi] = dl > 0.f ? (m_ref * c + log2_hw(dl)) * kLn2 : kNegInf;
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-  const int BH = a.B * a.H;
-  const int nqt = (a.N + kBM - 1) / kBM;
-  const int64_t blocks = int64_t(BH) * nqt;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // Dense: one unit per (b, h). Packed: one per (h, sequence), B = sequence count.
+  const int64_t U = int64_t(a.B) * a.H;
+  const int rows = a.cu_seqlens ? a.max_seqlen : a.N;
+  const int nqt = (rows + kBM - 1) / kBM;
+  const int64_t blocks = U * nqt;
+  if (blocks > 0x7fffffff || U > 0x7fffffff) return hipErrorInvalidValue;
+  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreads), 0,
                      s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.o, a.lse, a.N, BH, nqt,
-                     a.scale * kLog2e);
+                     static_cast<const uint16_t*>(a.v), a.o, a.lse, a.N, int(U), nqt,
+                     a.scale * kLog2e, a.window_left, a.window_right, a.cu_seqlens,
+                     a.cu_seqlens ? a.B : 1, a.max_seqlen);
   return hipGetLastError();
 }
 

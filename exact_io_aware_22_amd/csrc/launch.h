@@ -16,6 +16,9 @@ struct FwdArgs {
   int B, H, N, D;
   float scale;
   bool causal;
+  int window_left = -1, window_right = -1;  // -1: unbounded on that side
+  const int* cu_seqlens = nullptr;          // packed sequences (device), B + 1 entries
+  int max_seqlen = 0;
 };
 
 struct DecodeArgs {

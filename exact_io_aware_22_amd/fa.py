@@ -23,7 +23,8 @@ _lib = None
 
 FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
-EXPORTED = ("fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_backward",
+EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
+            "fa_backward",
             "fa_strerror", "fa_abi_version")
 
 
@@ -44,6 +45,8 @@ def load():
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_forward.restype = i
+    lib.fa_forward_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, i, i, vp]
+    lib.fa_forward_ext.restype = i
     lib.fa_decode_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_decode_partials.restype = i
     lib.fa_combine_partials.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
@@ -99,6 +102,26 @@ def fa_forward(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None
     _check(code, "fa_forward")
 
 
+def fa_forward_ext(q, k, v, o, lse, scale: float, causal: bool, window_left: int = -1,
+                   window_right: int = -1, cu_seqlens=None, max_seqlen: int = 0,
+                   stream=None) -> None:
+    """Dense: as fa_forward, plus the window. Packed (cu_seqlens, an int32 device tensor
+    of nseq + 1 offsets): q, k, v, o [H, total, D], lse [H, total]."""
+    _dense(q, k, v, o, lse, cu_seqlens)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        H, N, D = q.shape
+        B = cu_seqlens.numel() - 1
+    else:
+        B, H, N, D = q.shape
+    code = load().fa_forward_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
+                                 float(scale), int(bool(causal)), int(window_left),
+                                 int(window_right), _ptr(cu_seqlens), int(max_seqlen),
+                                 _dtype_code(q), _stream(stream))
+    _check(code, "fa_forward_ext")
+
+
 def fa_decode_partials(q, k, v, m, d, o_part, scale: float, splits: int, stream=None) -> None:
     """q: [B, H, 1, D] or [B, H, D]; k, v: [B, H, L, D]; m, d: [B*H, splits]; o_part: [B*H, splits, D]."""
     _dense(q, k, v, m, d, o_part)
@@ -142,6 +165,26 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, stream=No
     o = torch.empty(B, H, N, D, dtype=torch.float32, device=q.device)
     lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     fa_forward(q, k, v, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def forward_ext(q, k, v, scale: float | None = None, causal: bool = False,
+                window_left: int = -1, window_right: int = -1, cu_seqlens=None,
+                max_seqlen: int | None = None, stream=None):
+    """Allocate O (q's shape, fp32) and lse (q's shape without D, fp32) and run
+    fa_forward_ext. Packed (cu_seqlens given): q, k, v [H, total, D]; max_seqlen
+    defaults to the longest sequence (read from cu_seqlens on the host). Rows that no
+    sequence covers are left unwritten."""
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if cu_seqlens is not None and max_seqlen is None:
+        c = cu_seqlens.cpu()
+        max_seqlen = int((c[1:] - c[:-1]).max()) if c.numel() > 1 else 0
+    o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    fa_forward_ext(q, k, v, o, lse, scale, causal, window_left, window_right, cu_seqlens,
+                   max_seqlen or 0, stream)
     return o, lse
 
 

@@ -47,10 +47,12 @@ enum {
   FA_ERR_NULL = -1,  /* a required pointer is NULL                                  */
   FA_ERR_SHAPE = -2, /* negative size, D not in {64, 128}, splits < 1, or a size
                         whose element count does not fit in 63 bits                 */
-  FA_ERR_DTYPE = -3, /* dtype is neither FA_F32 nor FA_BF16                         */
+  FA_ERR_DTYPE = -3, /* dtype is neither FA_F32 nor FA_BF16 (or FA_F32 with a
+                        window or packed sequences)                                 */
   FA_ERR_ALIGN = -4, /* a tensor pointer is not 16-byte aligned; m, d, lse or delta
                         not 4-byte aligned                                          */
-  FA_ERR_ARG = -5,   /* scale not finite or not > 0, or causal not 0 or 1           */
+  FA_ERR_ARG = -5,   /* scale not finite or not > 0, causal not 0 or 1, or a window
+                        bound below -1                                              */
   FA_ERR_HIP = -6    /* the HIP runtime rejected the kernel launch                   */
 };
 
@@ -70,6 +72,37 @@ enum {
 int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                int B, int H, int N, int D, float scale, int causal, int dtype,
                void* stream);
+
+/*
+ * fa_forward_ext -- fa_forward with mask variants: a sliding window and packed
+ * variable-length sequences. Masked keys enter as the identity of the fold (score
+ * -inf, weight 0; sections "Associativity is All You Need" and "Why Attention's
+ * Combine Still Associates"), and key tiles wholly outside a row block's window are
+ * not visited at all.
+ *
+ *   window_left, window_right : key j is visible to query i iff
+ *             i - window_left <= j <= i + window_right; -1 leaves that side
+ *             unbounded (other negative values: FA_ERR_ARG). causal = 1 also bounds
+ *             the right side at 0 (j <= i).
+ *   cu_seqlens : NULL for the dense layout of fa_forward. Otherwise a DEVICE array of
+ *             B + 1 int32 offsets (nondecreasing, cu_seqlens[0] = 0,
+ *             cu_seqlens[B] <= N): B packed sequences, sequence s owning rows
+ *             [cu_seqlens[s], cu_seqlens[s+1]) of every head; q, k, v and o are then
+ *             [H][N][D] and lse is [H][N], and each sequence attends only to itself
+ *             (positions counted from its first row). Offsets are clamped into
+ *             [0, N] on the device, so inconsistent contents cannot make the library
+ *             touch memory outside the tensors.
+ *   max_seqlen : packed only: an upper bound on every sequence length. A longer
+ *             sequence is taken as its first max_seqlen rows (they attend to those rows
+ *             only) and its later rows are left unwritten; rows past cu_seqlens[B] are
+ *             never written.
+ * Windows and packed sequences need dtype FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
+ * fa_forward(...) is fa_forward_ext(..., -1, -1, NULL, 0, ...).
+ */
+int fa_forward_ext(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                   int H, int N, int D, float scale, int causal, int window_left,
+                   int window_right, const int* cu_seqlens, int max_seqlen, int dtype,
+                   void* stream);
 
 /*
  * fa_decode_partials -- split-KV single-query attention, first step.

@@ -35,8 +35,8 @@ def lib():
 
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
-        ["fa_forward", "fa_decode_partials", "fa_combine_partials", "fa_backward", "fa_strerror",
-         "fa_abi_version"])
+        ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
+         "fa_backward", "fa_strerror", "fa_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -83,6 +83,31 @@ def test_forward_validation(lib):
     assert fwd(lib, H=0, D=128, dtype=0) == OK
     assert fwd(lib, q=None, k=None, v=None, o=None, lse=None, N=0) == OK  # empty tensors
     assert fwd(lib, N=0, D=80) == SHAPE  # sizes are still checked first
+
+
+def fwx(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=8, D=64, scale=0.125, causal=0, wl=-1,
+        wr=-1, cu=None, max_seqlen=0, dtype=1):
+    return lib.fa_forward_ext(q, k, v, o, lse, B, H, N, D, scale, causal, wl, wr, cu,
+                              max_seqlen, dtype, None)
+
+
+def test_forward_ext_validation(lib):
+    for wl, wr in ((-2, -1), (-1, -7), (-5, 3)):
+        assert fwx(lib, wl=wl, wr=wr) == ARG
+    assert fwx(lib, wl=3, dtype=0) == DTYPE  # windows need bf16
+    assert fwx(lib, cu=P, max_seqlen=8, dtype=0) == DTYPE  # packed needs bf16
+    assert fwx(lib, cu=P, max_seqlen=-1) == SHAPE
+    assert fwx(lib, cu=P + 2, max_seqlen=8) == ALIGN
+    assert fwx(lib, cu=P, max_seqlen=8, lse=None) == NULL
+    assert fwx(lib, wl=4, wr=0, q=P + 8) == ALIGN
+    # packed size check is on H x N x D: B counts sequences and may be large
+    assert fwx(lib, B=1 << 30, H=4, N=1 << 10, cu=P, max_seqlen=0) == OK
+    assert fwx(lib, B=1 << 30, H=1 << 30, N=1 << 30) == SHAPE
+    # empty problems: no pointer is touched
+    assert fwx(lib, cu=P, max_seqlen=0, q=None, k=None, v=None, o=None, lse=None) == OK
+    assert fwx(lib, N=0, wl=5, q=None) == OK
+    assert fwx(lib, B=0, cu=P, max_seqlen=4) == OK  # no sequences
+    assert fwx(lib, N=0, D=72) == SHAPE
 
 
 def dec(lib, q=P, k=P, v=P, m=P, d=P, op=P, B=1, H=1, L=64, D=128, scale=0.1, splits=4, dtype=1):
