@@ -34,6 +34,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 HEADLINE = "large_score_causal_d128"
 DECODE = "split_kv_decode"
+MASKED = ["sliding_window_4096_causal_d128", "sliding_window_1024_causal_d128",
+          "varlen_causal_d128"]
 EXTRA = ["batched_prefill_d64", "batched_prefill_d64_causal", "long_context_causal_32768",
          "long_context_causal_32767"]
 KERNEL_SOURCES = {
@@ -269,6 +271,63 @@ def bench_backward(steps: int, warmup: int, torch, fa, make_inputs, W, check: bo
     return res
 
 
+def bench_masks(steps: int, warmup: int, torch, fa, W, check: bool):
+    """fa_forward_ext on the sliding-window and packed workloads; flops count the
+    visible (query, key) pairs only (4*D per pair), so a window that skips tiles is
+    not credited for work it does not do. With `check`, one head (the window cases) or
+    the longest sequence of the last head (packed) is compared with the oracle."""
+    import numpy as np
+
+    from exact_io_aware_22_amd.workloads import make_inputs, packed_inputs
+
+    res = []
+    for name in MASKED:
+        w = W[name]
+        log(f"timing {name}")
+        if w.seqlens:
+            q, k, v, cu = packed_inputs(w)
+            cud = cu.cuda()
+            max_len = max(w.seqlens)
+        else:
+            q, k, v = make_inputs(w)
+            cu, cud, max_len = None, None, 0
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+        ms = time_launches(lambda: fa.fa_forward_ext(qd, kd, vd, o, lse, w.scale, w.causal,
+                                                     w.window_left, w.window_right, cud,
+                                                     max_len), steps, warmup, torch)
+        flops = w.flops()
+        r = {"workload": name, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+             "visible_pairs": w.visible_pairs(), "algorithmic_flops_per_launch": flops}
+        r["frac_of_bf16_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
+        if check:
+            import oracle
+
+            if w.seqlens:
+                h, s = w.H - 1, int(np.argmax(w.seqlens))
+                a, b = int(cu[s]), int(cu[s + 1])
+                o_ref, l_ref = oracle.attention_window(
+                    q[h:h + 1, a:b][None], k[h:h + 1, a:b][None], v[h:h + 1, a:b][None],
+                    w.scale, w.causal, w.window_left, w.window_right)
+                og = o[h:h + 1, a:b].cpu().double().numpy()[None]
+                lg = lse[h:h + 1, a:b].cpu().double().numpy()[None]
+                where = {"head": h, "sequence": s, "rows": b - a}
+            else:
+                sl = (slice(w.B - 1, w.B), slice(w.H - 1, w.H))
+                o_ref, l_ref = oracle.attention_window(q[sl], k[sl], v[sl], w.scale, w.causal,
+                                                       w.window_left, w.window_right)
+                og, lg = o[sl].cpu().double().numpy(), lse[sl].cpu().double().numpy()
+                where = {"head": [w.B - 1, w.H - 1], "rows": w.N}
+            r["parity"] = dict(where, max_abs_err_o=float(np.max(np.abs(og - o_ref))),
+                               max_abs_err_lse=float(np.max(np.abs(lg - l_ref))), tol_o=2e-2,
+                               tol_lse=1e-3)
+        res.append(r)
+        del qd, kd, vd, o, lse, cud
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(torch, nbytes: int, steps: int):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -284,7 +343,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "masks", "copy"],
                     default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -352,6 +411,9 @@ def main() -> int:
         log(f"timing the backward on {HEADLINE}")
         out["backward"] = bench_backward(max(3, args.steps // 5), max(2, args.warmup // 10), torch,
                                          fa, make_inputs, WORKLOADS, check=args.only == "all")
+    if args.only in ("all", "masks"):
+        out["masks"] = bench_masks(max(3, args.steps // 2), max(2, args.warmup // 4), torch, fa,
+                                   WORKLOADS, check=args.only in ("all", "masks"))
     if args.only in ("all", "decode"):
         log(f"timing {DECODE}")
         out["decode"] = bench_decode(args.steps, args.warmup, torch, fa, make_inputs, WORKLOADS)

@@ -106,7 +106,7 @@ __device__ __forceinline__ void map_tile(int bid, int BH, int nqt, bool causal, 
 }
 
 // Dense: units are the B*H heads of [B][H][Ntot][D] tensors. Packed (cu != nullptr):
-// units are (head, sequence) pairs of [H][Ntot][D] tensors, sequence s owning rows
+// units are (sequence, head) pairs of [H][Ntot][D] tensors, sequence s owning rows
 // [cu[s], cu[s+1]) (values clamped into [0, Ntot], length capped at max_len).
 // Window: key j visible to query i iff i - wl <= j <= i + wr (negative = unbounded);
 // causal is the wr = 0 case.
@@ -129,7 +129,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   int N;            // rows of this unit
   int64_t row0;     // its first row within the [.][Ntot] row space
   if (cu != nullptr) {
-    const int h = unit / nseq, sq = unit % nseq;
+    // Sequence-major units: the heads of one sequence are consecutive units, so the
+    // round-robin over XCDs spreads every sequence's heads evenly over the XCDs and
+    // each XCD gets the same share of long and short sequences.
+    const int nh = U / nseq, sq = unit / nh, h = unit % nh;
     const int a = min(max(cu[sq], 0), Ntot), b = min(max(cu[sq + 1], a), Ntot);
     N = min(b - a, max_len);
     row0 = int64_t(h) * Ntot + a;
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-  // Dense: one unit per (b, h). Packed: one per (h, sequence), B = sequence count.
+  // Dense: one unit per (b, h). Packed: one per (sequence, h), B = sequence count.
   const int64_t U = int64_t(a.B) * a.H;
   const int rows = a.cu_seqlens ? a.max_seqlen : a.N;
   const int nqt = (rows + kBM - 1) / kBM;

@@ -34,6 +34,9 @@ class Workload:
     sigma_qk: float = 1.0
     sigma_v: float = 1.0
     splits: int = 0  # split-KV decode only: number of key chunks
+    window_left: int = -1   # sliding window: key j visible to query i iff
+    window_right: int = -1  # i - window_left <= j <= i + window_right (-1: unbounded)
+    seqlens: tuple = ()     # packed batch: sequence lengths (then B = len, N = sum)
     note: str = field(default="", compare=False)
 
     @property
@@ -41,10 +44,41 @@ class Workload:
         """1/sqrt(D), rounded to float32 (the value the library receives)."""
         return float(torch.tensor(1.0 / math.sqrt(self.D), dtype=torch.float32))
 
+    @property
+    def masked(self) -> bool:
+        return bool(self.seqlens) or self.window_left >= 0 or self.window_right >= 0
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs a row may see, summed over rows and heads."""
+        if self.seqlens:
+            return self.H * sum(_pairs(n, self.causal, self.window_left, self.window_right)
+                                for n in self.seqlens)
+        return self.B * self.H * _pairs(self.N, self.causal, self.window_left,
+                                        self.window_right)
+
     def flops(self) -> float:
-        """Attention flops, 4*B*H*N*L*D, halved for causal (the usual convention)."""
+        """Attention flops: 4*B*H*N*L*D, halved for causal (the usual convention); for a
+        window or a packed batch, 4*D per visible (query, key) pair."""
+        if self.masked:
+            return 4.0 * self.D * self.visible_pairs()
         f = 4.0 * self.B * self.H * self.N * self.L * self.D
         return f / 2.0 if self.causal else f
+
+
+def _pairs(n: int, causal: bool, wl: int, wr: int) -> int:
+    """Number of (i, j) in [0, n)^2 with max(0, i - wl) <= j <= min(n - 1, i + wr)."""
+    i = torch.arange(n, dtype=torch.int64)
+    lo = torch.clamp(i - wl, min=0) if wl >= 0 else torch.zeros_like(i)
+    r = 0 if causal else wr
+    hi = torch.clamp(i + r, max=n - 1) if r >= 0 else torch.full_like(i, n - 1)
+    return int(torch.clamp(hi - lo + 1, min=0).sum())
+
+
+def _seqlens(seed: int, count: int, lo: int, hi: int) -> tuple:
+    """`count` sequence lengths drawn uniformly from [lo, hi] with a seeded generator."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (count,), generator=gen))
 
 
 def _catalog():
@@ -64,7 +98,17 @@ def _catalog():
                  note="long context, N a multiple of every tile"),
         Workload("long_context_causal_32767", 1, 16, 32767, 32767, 128, bf16, True, 5,
                  note="long context, ragged tail"),
+        Workload("sliding_window_4096_causal_d128", 2, 32, 8192, 8192, 128, bf16, True, 3,
+                 sigma_qk=3.0, window_left=4095,
+                 note="the large-score inputs; each query sees itself and 4095 keys before it"),
+        Workload("sliding_window_1024_causal_d128", 2, 32, 8192, 8192, 128, bf16, True, 3,
+                 sigma_qk=3.0, window_left=1023,
+                 note="the large-score inputs; each query sees itself and 1023 keys before it"),
     ]
+    lens = _seqlens(6, 32, 64, 4032)
+    w.append(Workload("varlen_causal_d128", len(lens), 32, sum(lens), sum(lens), 128, bf16,
+                      True, 6, seqlens=lens,
+                      note="packed batch of 32 causal sequences, lengths uniform in [64, 4032]"))
     return {x.name: x for x in w}
 
 
@@ -104,6 +148,22 @@ def make_inputs(w: Workload | str, B: int | None = None, H: int | None = None,
     k = _draw(gen, (B, H), L, w.D, w.sigma_qk, w.dtype)
     v = _draw(gen, (B, H), L, w.D, w.sigma_v, w.dtype)
     return q, k, v
+
+
+def packed_inputs(w: Workload | str):
+    """A packed batch: q, k, v [H, total, D] (every head's rows drawn by the recipe above,
+    head by head) and cu_seqlens [nseq + 1] int32 offsets, all on the CPU."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    total = sum(w.seqlens)
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed)
+    q = _draw(gen, (w.H,), total, w.D, w.sigma_qk, w.dtype)
+    k = _draw(gen, (w.H,), total, w.D, w.sigma_qk, w.dtype)
+    v = _draw(gen, (w.H,), total, w.D, w.sigma_v, w.dtype)
+    cu = torch.zeros(len(w.seqlens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(w.seqlens, dtype=torch.int64), 0).to(torch.int32)
+    return q, k, v, cu
 
 
 def random_tensor(shape, seed: int, dtype=torch.bfloat16, sigma: float = 1.0) -> torch.Tensor:
