@@ -1,4 +1,5 @@
-"""fp64 CPU oracle (test infrastructure only; see oracle.fp64 and oracle.backward)."""
+"""fp64 CPU oracle (test infrastructure only; see oracle.fp64, oracle.backward,
+oracle.masks and oracle.monoids)."""
 from .fp64 import (  # noqa: F401
     LOG2E,
     NEG_INF,
@@ -18,3 +19,4 @@ from .fp64 import (  # noqa: F401
 )
 from .backward import attention_backward  # noqa: F401,E402
 from .masks import attention_varlen, attention_window, visible  # noqa: F401,E402
+from .monoids import log_sum_exp, moments, softmax_stats, variance  # noqa: F401,E402
