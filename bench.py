@@ -41,6 +41,8 @@ EXTRA = ["batched_prefill_d64", "batched_prefill_d64_causal", "long_context_caus
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": "exact_io_aware_22_amd/csrc/fwd_bf16.hip",
     "decode_partials_kernel": "exact_io_aware_22_amd/csrc/decode.hip",
+    "row_reduce_kernel<SoftmaxMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
+    "row_reduce_kernel<WelfordMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
 }
 
 
@@ -328,6 +330,54 @@ def bench_masks(steps: int, warmup: int, torch, fa, W, check: bool):
     return res
 
 
+def bench_reductions(steps: int, warmup: int, torch, fa, check: bool):
+    """fa_softmax_stats and fa_moments on their 1 GiB workloads: HBM-bound, so GB/s of
+    algorithmic bytes (every element read once, two float32 outputs per row written)
+    against 8 TB/s; with `check`, 64 seeded rows compared with the oracle."""
+    import numpy as np
+
+    from exact_io_aware_22_amd.workloads import ROW_WORKLOADS, make_rows
+
+    res = []
+    for name in sorted(ROW_WORKLOADS):
+        w = ROW_WORKLOADS[name]
+        log(f"timing {name}")
+        x = make_rows(w)
+        xd = x.cuda()
+        a = torch.empty(w.rows, device="cuda")
+        b = torch.empty(w.rows, device="cuda")
+        softmax = name.startswith("softmax")
+        fn = fa.fa_softmax_stats if softmax else fa.fa_moments
+        ms = time_launches(lambda: fn(xd, a, b), steps, warmup, torch)
+        nbytes = w.bytes_read() + w.bytes_written()
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        kernel = "row_reduce_kernel<" + ("SoftmaxMonoid" if softmax else "WelfordMonoid") + ">"
+        r = {"workload": name, "rows": w.rows, "n": w.n, "dtype": str(w.dtype).split(".")[-1],
+             "ms": ms, "value": gbs, "unit": "GB/s",
+             "roofline": {"kernel": kernel, "bound": "hbm", "achieved": gbs,
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                          "traffic": measured_traffic(kernel, name),
+                          "algorithmic_bytes_per_launch": nbytes}}
+        if check:
+            import oracle
+
+            rows = np.random.default_rng(5).choice(w.rows, 64, replace=False)
+            sub = x[torch.as_tensor(rows)]
+            ga, gb = a.cpu().double().numpy()[rows], b.cpu().double().numpy()[rows]
+            if softmax:
+                m_ref, d_ref = oracle.softmax_stats(sub)
+                r["parity"] = {"rows": 64, "m_exact": bool(np.array_equal(ga, m_ref)),
+                               "max_rel_err_d": float(np.max(np.abs(gb - d_ref) / d_ref))}
+            else:
+                _, mu_ref, m2_ref = oracle.moments(sub)
+                r["parity"] = {"rows": 64, "max_abs_err_mean": float(np.max(np.abs(ga - mu_ref))),
+                               "max_rel_err_m2": float(np.max(np.abs(gb - m2_ref) / m2_ref))}
+        res.append(r)
+        del x, xd, a, b
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(torch, nbytes: int, steps: int):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -343,7 +393,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "masks", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "masks",
+                                       "reductions", "copy"],
                     default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -414,6 +465,9 @@ def main() -> int:
     if args.only in ("all", "masks"):
         out["masks"] = bench_masks(max(3, args.steps // 2), max(2, args.warmup // 4), torch, fa,
                                    WORKLOADS, check=args.only in ("all", "masks"))
+    if args.only in ("all", "reductions"):
+        out["reductions"] = bench_reductions(args.steps, args.warmup, torch, fa,
+                                             check=args.only in ("all", "reductions"))
     if args.only in ("all", "decode"):
         log(f"timing {DECODE}")
         out["decode"] = bench_decode(args.steps, args.warmup, torch, fa, make_inputs, WORKLOADS)

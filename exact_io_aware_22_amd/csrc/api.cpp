@@ -133,3 +133,33 @@ int fa_combine_partials(const float* m, const float* d, const float* o_part, int
 }
 
 }  // extern "C"
+
+namespace {
+
+// Shared validation of the two row reductions: x [rows][n] of dtype; out0, out1 [rows].
+int row_reduce(const void* x, float* out0, float* out1, int rows, int n, int dtype, void* stream,
+               hipError_t (*launch)(const fa::RowReduceArgs&, hipStream_t)) {
+  if (rows < 0 || n < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (rows == 0) return FA_OK;  // empty: no pointer is touched
+  if (!out0 || !out1 || (n > 0 && !x)) return FA_ERR_NULL;
+  if (!aligned(x, dtype == FA_BF16 ? 2 : 4) || !aligned(out0, 4) || !aligned(out1, 4))
+    return FA_ERR_ALIGN;
+  fa::RowReduceArgs a{x, rows, n, dtype == FA_BF16, out0, out1};
+  return hip_status(launch(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_softmax_stats(const void* x, float* m, float* d, int rows, int n, int dtype,
+                     void* stream) {
+  return row_reduce(x, m, d, rows, n, dtype, stream, fa::launch_softmax_stats);
+}
+
+int fa_moments(const void* x, float* mean, float* m2, int rows, int n, int dtype, void* stream) {
+  return row_reduce(x, mean, m2, rows, n, dtype, stream, fa::launch_moments);
+}
+
+}  // extern "C"

@@ -58,6 +58,15 @@ struct BwdArgs {
   bool causal;
 };
 
+struct RowReduceArgs {
+  const void* x;  // [rows][n], float32 or bfloat16
+  int64_t rows;
+  int n;
+  bool bf16;
+  float* out0;  // softmax: m; moments: mean
+  float* out1;  // softmax: d; moments: M2
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode_partials_bf16(const DecodeArgs& a, hipStream_t s);
@@ -65,5 +74,7 @@ hipError_t launch_decode_partials_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine_partials(const CombineArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_softmax_stats(const RowReduceArgs& a, hipStream_t s);
+hipError_t launch_moments(const RowReduceArgs& a, hipStream_t s);
 
 }  // namespace fa

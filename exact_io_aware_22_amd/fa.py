@@ -24,8 +24,7 @@ _lib = None
 FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
-            "fa_backward",
-            "fa_strerror", "fa_abi_version")
+            "fa_backward", "fa_softmax_stats", "fa_moments", "fa_strerror", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -47,6 +46,10 @@ def load():
     lib.fa_forward.restype = i
     lib.fa_forward_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, i, i, vp]
     lib.fa_forward_ext.restype = i
+    lib.fa_softmax_stats.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.fa_softmax_stats.restype = i
+    lib.fa_moments.argtypes = [vp, vp, vp, i, i, i, vp]
+    lib.fa_moments.restype = i
     lib.fa_decode_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_decode_partials.restype = i
     lib.fa_combine_partials.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
@@ -156,7 +159,48 @@ def fa_backward(q, k, v, o, lse, dout, delta, dq, dk, dv, scale: float, causal: 
     _check(code, "fa_backward")
 
 
+def _rows(x, out0, out1):
+    _dense(x, out0, out1)
+    if x.dim() < 1:
+        raise ValueError("x needs at least one dimension (its rows are along the last)")
+    n, rows = x.shape[-1], math.prod(x.shape[:-1])
+    if out0.numel() != rows or out1.numel() != rows:
+        raise ValueError(f"outputs must hold one value per row ({rows})")
+    return rows, n
+
+
+def fa_softmax_stats(x, m, d, stream=None) -> None:
+    """x: [..., n] (bf16 or fp32); m, d: fp32 with one element per row of x."""
+    rows, n = _rows(x, m, d)
+    code = load().fa_softmax_stats(_ptr(x), _ptr(m), _ptr(d), rows, n, _dtype_code(x),
+                                   _stream(stream))
+    _check(code, "fa_softmax_stats")
+
+
+def fa_moments(x, mean, m2, stream=None) -> None:
+    """x: [..., n] (bf16 or fp32); mean, m2: fp32 with one element per row of x."""
+    rows, n = _rows(x, mean, m2)
+    code = load().fa_moments(_ptr(x), _ptr(mean), _ptr(m2), rows, n, _dtype_code(x),
+                             _stream(stream))
+    _check(code, "fa_moments")
+
+
 # ------------------------------------------------------------------ conveniences
+def softmax_stats(x, stream=None):
+    """Allocate m, d (x's shape without its last dim, fp32) and run fa_softmax_stats."""
+    m = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    d = torch.empty_like(m)
+    fa_softmax_stats(x, m, d, stream)
+    return m, d
+
+
+def moments(x, stream=None):
+    """Allocate mean, m2 (x's shape without its last dim, fp32) and run fa_moments."""
+    mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    m2 = torch.empty_like(mean)
+    fa_moments(x, mean, m2, stream)
+    return mean, m2
+
 def forward(q, k, v, scale: float | None = None, causal: bool = False, stream=None):
     """Allocate O [B, H, N, D] fp32 and lse [B, H, N] fp32 and run fa_forward."""
     B, H, N, D = q.shape

@@ -166,6 +166,51 @@ def packed_inputs(w: Workload | str):
     return q, k, v, cu
 
 
+@dataclass(frozen=True)
+class RowWorkload:
+    """A [rows, n] matrix for the row reductions: offset + sigma * N(0, 1) in float32,
+    cast to dtype, drawn 1024 rows at a time from one seeded generator."""
+    name: str
+    rows: int
+    n: int
+    dtype: torch.dtype
+    seed: int
+    sigma: float = 1.0
+    offset: float = 0.0
+    note: str = field(default="", compare=False)
+
+    def bytes_read(self) -> int:
+        return self.rows * self.n * torch.finfo(self.dtype).bits // 8
+
+    def bytes_written(self) -> int:
+        return self.rows * 2 * 4  # two float32 outputs per row
+
+
+ROW_WORKLOADS = {w.name: w for w in [
+    RowWorkload("softmax_stats_logits_fp32", 8192, 32768, torch.float32, 7, sigma=8.0,
+                note="8192 rows of 32768 float32 logits, N(0, 64): scores in the tens"),
+    RowWorkload("moments_activations_bf16", 65536, 8192, torch.bfloat16, 8, sigma=1.0,
+                offset=3.0, note="65536 rows of 8192 bf16 activations, 3 + N(0, 1)"),
+]}
+
+
+def make_rows(w: RowWorkload | str, rows: int | None = None) -> torch.Tensor:
+    """x [rows, n] on the CPU, by the RowWorkload recipe (the first `rows` rows)."""
+    if isinstance(w, str):
+        w = ROW_WORKLOADS[w]
+    rows = w.rows if rows is None else rows
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed)
+    out = torch.empty(rows, w.n, dtype=w.dtype)
+    s = torch.tensor(w.sigma, dtype=torch.float32)
+    o = torch.tensor(w.offset, dtype=torch.float32)
+    for r0 in range(0, rows, 1024):
+        r1 = min(rows, r0 + 1024)
+        x = torch.randn(r1 - r0, w.n, generator=gen, dtype=torch.float32)
+        out[r0:r1] = (x * s + o).to(w.dtype)
+    return out
+
+
 def random_tensor(shape, seed: int, dtype=torch.bfloat16, sigma: float = 1.0) -> torch.Tensor:
     """A seeded N(0, sigma^2) tensor of any shape (for edge-case tests)."""
     gen = torch.Generator(device="cpu")

@@ -1,6 +1,6 @@
 /*
- * fa.h -- C ABI of libfa.so: exact tiled attention forward, its backward, and
- * split-KV decode for AMD Instinct MI355X (gfx950).
+ * fa.h -- C ABI of libfa.so: exact tiled attention forward, its backward, split-KV
+ * decode, and row reductions on the same schedule, for AMD Instinct MI355X (gfx950).
  *
  * What is computed (definitions from "Learning FlashAttention the Hard Way --
  * Part 1", cloudrift.ai):
@@ -50,7 +50,8 @@ enum {
   FA_ERR_DTYPE = -3, /* dtype is neither FA_F32 nor FA_BF16 (or FA_F32 with a
                         window or packed sequences)                                 */
   FA_ERR_ALIGN = -4, /* a tensor pointer is not 16-byte aligned; m, d, lse or delta
-                        not 4-byte aligned                                          */
+                        not 4-byte aligned; a row-reduction input not aligned to its
+                        element                                                     */
   FA_ERR_ARG = -5,   /* scale not finite or not > 0, causal not 0 or 1, or a window
                         bound below -1                                              */
   FA_ERR_HIP = -6    /* the HIP runtime rejected the kernel launch                   */
@@ -165,6 +166,37 @@ int fa_combine_partials(const float* m, const float* d, const float* o_part, int
 int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
                 const void* dout, float* delta, float* dq, float* dk, float* dv, int B, int H,
                 int N, int D, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Row reductions on the same schedule as the attention fold, with another combine
+ * (section "Associativity is All You Need": only the combine changes, never the
+ * schedule). Both read x as [rows][n] elements of `dtype` (float32 or bfloat16),
+ * dense and row-major, each element once; x needs only element alignment (2 or 4
+ * bytes), the outputs 4 bytes. rows = 0 is an empty call (no pointer touched); n = 0
+ * writes the identity state for every row (x may then be NULL). Accumulation is
+ * float32.
+ */
+
+/*
+ * fa_softmax_stats -- the online-softmax normaliser of every row (section "Online
+ * Softmax Reparametrization"): the state (m, d) of the row, m = max_j x_j (exactly one
+ * of the inputs) and d = sum_j e^{x_j - m}, so ln sum_j e^{x_j} = m + ln d and the
+ * softmax of the row is e^{x_j - m} / d. -inf entries are the identity and add
+ * nothing; a row of only -inf (or n = 0) is written as (-inf, 0).
+ *   m, d : [rows] float32, written.
+ */
+int fa_softmax_stats(const void* x, float* m, float* d, int rows, int n, int dtype,
+                     void* stream);
+
+/*
+ * fa_moments -- Welford's moments of every row in the pairwise form of Chan, Golub and
+ * LeVeque (section "The Same Move: Welford's Variance"): the state (n, mu, M2) with
+ * mu = (1/n) sum_j x_j and M2 = sum_j (x_j - mu)^2; the population variance is M2 / n,
+ * the sample variance M2 / (n - 1). n is the row length and is not written; n = 0
+ * writes mean = M2 = 0 (the identity).
+ *   mean, m2 : [rows] float32, written.
+ */
+int fa_moments(const void* x, float* mean, float* m2, int rows, int n, int dtype, void* stream);
 
 /* Static, human-readable name of an FA_* code (never NULL). */
 const char* fa_strerror(int code);

@@ -36,7 +36,7 @@ def lib():
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
-         "fa_backward", "fa_strerror", "fa_abi_version"])
+         "fa_backward", "fa_softmax_stats", "fa_moments", "fa_strerror", "fa_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -171,3 +171,22 @@ def test_backward_validation(lib):
 def test_binding_raises_with_message(lib):
     with pytest.raises(fa.FaError, match="scale"):
         fa._check(lib.fa_forward(P, P, P, P, P, 1, 1, 8, 64, -1.0, 0, 1, None), "fa_forward")
+
+
+def red(lib, which, x=P, o0=P, o1=P, rows=4, n=100, dtype=1):
+    return getattr(lib, which)(x, o0, o1, rows, n, dtype, None)
+
+
+@pytest.mark.parametrize("which", ["fa_softmax_stats", "fa_moments"])
+def test_row_reduction_validation(lib, which):
+    assert red(lib, which, x=None) == NULL
+    assert red(lib, which, o0=None) == NULL
+    assert red(lib, which, o1=None) == NULL
+    assert red(lib, which, rows=-1) == SHAPE
+    assert red(lib, which, n=-5) == SHAPE
+    assert red(lib, which, dtype=3) == DTYPE
+    assert red(lib, which, x=P + 1) == ALIGN          # bf16 needs 2-byte alignment
+    assert red(lib, which, x=P + 2, dtype=0) == ALIGN  # fp32 needs 4
+    assert red(lib, which, o1=P + 2) == ALIGN
+    assert red(lib, which, rows=0, x=None, o0=None, o1=None) == OK  # empty
+    assert red(lib, which, rows=0, n=-1) == SHAPE                    # sizes first
