@@ -34,10 +34,13 @@
 namespace fa {
 namespace {
 
-constexpr int kWavesB = 4;                 // wavefronts per workgroup (one per SIMD)
+constexpr int kWavesB = 4;                 // dK/dV: wavefronts per workgroup (one per SIMD)
 constexpr int kThreadsB = 64 * kWavesB;
 constexpr int kRowsB = 32 * kWavesB;       // rows a workgroup owns (queries or keys)
 constexpr int kTile = 64;                  // rows per LDS tile (two 32-row blocks)
+// dQ: 8 wavefronts (two per SIMD, so one's element-wise work overlaps the other's
+// products) and 256 query rows per workgroup; it fits 256 VGPRs per wavefront.
+constexpr int kWavesQ = 8, kThreadsQ = 64 * kWavesQ, kRowsQ = 32 * kWavesQ;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 #define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
 
 // ------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreadsB, 1) void dq_kernel(
+__global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ dQ,
@@ -145,11 +148,11 @@ __global__ __launch_bounds__(kThreadsB, 1) void dq_kernel(
   const int64_t head = int64_t(bh) * N * D;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
-  const int q0 = qt * kRowsB, qw0 = q0 + 32 * wave, qrow = qw0 + l32;
+  const int q0 = qt * kRowsQ, qw0 = q0 + 32 * wave, qrow = qw0 + l32;
 
   const int nblk_all = (N + 31) >> 5;
   const int nblk = qw0 >= N ? 0 : (CAUSAL ? min(nblk_all, (qw0 >> 5) + 1) : nblk_all);
-  const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kRowsB) - 1) >> 5) + 1) : nblk_all;
+  const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kRowsQ) - 1) >> 5) + 1) : nblk_all;
   const int ntiles = (nblk_wg + 1) >> 1;
 
   // Own rows: Q^T and dO^T as B operands (k = head dims 16 c2 + 8 half + 0..7).
@@ -174,11 +177,12 @@ __global__ __launch_bounds__(kThreadsB, 1) void dq_kernel(
 
   // Staging: chunk i of a thread is row (tid + 256 i) / CPR, column (tid + 256 i) % CPR
   // of the 64-key tile; rows past the end read the last row (finite; masked below).
-  u32x4_t sk[G::SPT], sv[G::SPT];
+  constexpr int SPQ = kTile * G::CPR / kThreadsQ;  // 16-byte chunks per thread per tile
+  u32x4_t sk[SPQ], sv[SPQ];
   auto gload = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < G::SPT; ++i) {
-      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
+    for (int i = 0; i < SPQ; ++i) {
+      const int id = tid + kThreadsQ * i, r = id / G::CPR, col = id % G::CPR;
       const int64_t gr = min(t * kTile + r, N - 1);
       sk[i] = load16(Kh + gr * D + col * 8);
       sv[i] = load16(Vh + gr * D + col * 8);
@@ -187,8 +191,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void dq_kernel(
   auto lstore = [&](int slot) {
     uint8_t* s = smem + slot * SLOT;
 #pragma unroll
-    for (int i = 0; i < G::SPT; ++i) {
-      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
+    for (int i = 0; i < SPQ; ++i) {
+      const int id = tid + kThreadsQ * i, r = id / G::CPR, col = id % G::CPR;
       *reinterpret_cast<u32x4_t*>(s + r * G::RS + col * 16) = sk[i];
       *reinterpret_cast<u32x4_t*>(s + G::RT + r * G::CS + col * 16) = sk[i];
       *reinterpret_cast<u32x4_t*>(s + G::RT + G::CT + r * G::RS + col * 16) = sv[i];
@@ -439,15 +443,15 @@ hipError_t launch(const BwdArgs& a, hipStream_t s) {
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
   const int64_t dblocks = (rows + 15) / 16;
-  const int nt = (a.N + kRowsB - 1) / kRowsB;
-  const int64_t blocks = int64_t(BH) * nt;
+  const int nt = (a.N + kRowsB - 1) / kRowsB, ntq = (a.N + kRowsQ - 1) / kRowsQ;
+  const int64_t blocks = int64_t(BH) * nt, qblocks = int64_t(BH) * ntq;
   if (dblocks > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((delta_kernel<D>), dim3(unsigned(dblocks)), dim3(256), 0, s, dout, a.o,
                      a.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreadsB), 0, s, q, k,
-                     v, dout, a.lse, a.delta, a.dq, a.N, BH, nt, c, a.scale);
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(unsigned(qblocks)), dim3(kThreadsQ), 0, s, q,
+                     k, v, dout, a.lse, a.delta, a.dq, a.N, BH, ntq, c, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreadsB), 0, s, q,
