@@ -28,15 +28,26 @@
 // column-wise (transposing reads) is stored twice in LDS, with +16-byte rows for the
 // former and +64-byte rows for the latter: each padding keeps its own read pattern
 // free of bank conflicts on 64 banks, and no single padding serves both.
+// Staging: dq_kernel (8 wavefronts, 256 query rows) stages K and V through registers
+// into two LDS slots; dkdv_kernel (8 wavefronts at D = 64, 4 at D = 128) stages Q and
+// dO by direct global -> LDS loads, each into both of its layouts, so no registers
+// hold staged data. One barrier per 64-row tile in both.
 #include "device.h"
 #include "launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kWavesB = 4;                 // dK/dV: wavefronts per workgroup (one per SIMD)
-constexpr int kThreadsB = 64 * kWavesB;
-constexpr int kRowsB = 32 * kWavesB;       // rows a workgroup owns (queries or keys)
+// dK/dV: wavefronts per workgroup. At D = 64 eight (two per SIMD: one's element-wise
+// work overlaps the other's products); at D = 128 the two 32 x 128 accumulators and the
+// own K^T, V^T fragments leave too few of 256 VGPRs (it spills), so four (one per SIMD,
+// up to 512 registers).
+template <int D>
+struct KV {
+  static constexpr int kWaves = D == 64 ? 8 : 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = 32 * kWaves;  // key rows a workgroup owns
+};
 constexpr int kTile = 64;                  // rows per LDS tile (two 32-row blocks)
 // dQ: 8 wavefronts (two per SIMD, so one's element-wise work overlaps the other's
 // products) and 256 query rows per workgroup; it fits 256 VGPRs per wavefront.
@@ -58,7 +69,6 @@ struct BGeo {
   static constexpr int CS = D * 2 + 64;    // row stride, transposing-read copy
   static constexpr int RT = kTile * RS;
   static constexpr int CT = kTile * CS;
-  static constexpr int SPT = kTile * CPR / kThreadsB;  // 16-byte chunks per thread per tile
 };
 
 // Per-lane offsets of the two fragment read patterns (see the forward kernel):
@@ -265,7 +275,7 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
 
 // ------------------------------------------------------------------ dK, dV
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
+__global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ dK,
@@ -286,7 +296,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
   const uint16_t* dOh = dO + head;
   const float* lseh = LSE + int64_t(bh) * N;
   const float* delh = DELTA + int64_t(bh) * N;
-  const int k0 = kt * kRowsB, kw0 = k0 + 32 * wave, krow = kw0 + l32;
+  constexpr int kWavesB = KV<D>::kWaves;
+  const int k0 = kt * KV<D>::kRows, kw0 = k0 + 32 * wave, krow = kw0 + l32;
 
   // Query blocks this wavefront folds: [gs, nblk_all) (causal: from its diagonal).
   const int nblk_all = (N + 31) >> 5;
@@ -311,16 +322,62 @@ __global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
     dka[db] = f32x16_t{};
   }
 
-  u32x4_t sq[G::SPT], sd[G::SPT];
-  float sl = 0.f, sdl = 0.f;
-  auto gload = [&](int t) {
+  // Q and dO tiles reach LDS by direct global -> LDS loads (global_load_lds_dwordx4,
+  // as in the forward kernel), each into both of its layouts: one load moves 64 lanes x
+  // 16 bytes to 1 KB of consecutive LDS at M0 + 16 lane, and a padded tile is exactly
+  // CR (row layout) or CC (transposing layout) such kilobytes, so lane i of kilobyte j
+  // fills chunk 64 j + i, i.e. row (64 j + i) / C and column (64 j + i) % C; pad columns
+  // take a copy of column CPR - 1 and are never read. In a ragged tile, rows past the
+  // end take row N - 1 (finite; masked). Wavefront w issues kilobytes w, w + 8, w + 16.
+  // The 64 lse and Delta values of a tile go through registers (threads 0..63).
+  constexpr int CR = G::RS / 16, CC = G::CS / 16;
+  constexpr int MAXI = (CC + kWavesB - 1) / kWavesB;
+  static_assert(G::RT == CR * 1024 && G::CT == CC * 1024, "a padded tile is C kilobytes");
+  auto chunk_off = [&](int j, int C) -> uint32_t __attribute__((always_inline)) {
+    const int p = 64 * j + lane, r = p / C, col = min(p % C, G::CPR - 1);
+    return uint32_t(r * D * 2 + col * 16);
+  };
+  uint32_t offr[MAXI], offc[MAXI];
 #pragma unroll
-    for (int i = 0; i < G::SPT; ++i) {
-      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
-      const int64_t gr = min(t * kTile + r, N - 1);
-      sq[i] = load16(Qh + gr * D + col * 8);
-      sd[i] = load16(dOh + gr * D + col * 8);
+  for (int i = 0; i < MAXI; ++i) {
+    offr[i] = chunk_off(wave + kWavesB * i, CR);
+    offc[i] = chunk_off(wave + kWavesB * i, CC);
+  }
+  auto dma = [&](const uint16_t* src, const uint8_t* region, int C, const uint32_t (&d)[MAXI],
+                 int t) __attribute__((always_inline)) {
+    const uint64_t b64 = reinterpret_cast<uint64_t>(src) + uint64_t(t) * kTile * D * 2;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(
+        uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64))))) |
+        (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
+    const bool ragged = t * kTile + kTile > N;
+    const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(const uint8_t, region)));
+    constexpr int kRowShift = __builtin_ctz(2 * D);
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int j = wave + kWavesB * i;
+      if (j < C) {
+        uint32_t off = d[i];
+        if (ragged) {  // redirect rows past N - 1 to row N - 1
+          const int r = int(off >> kRowShift);
+          off -= uint32_t((r - (min(t * kTile + r, N - 1) - t * kTile)) << kRowShift);
+        }
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(m0), "v"(off), "s"(base)
+                     : "memory");
+      }
     }
+  };
+  // s_waitcnt vmcnt(0), through the builtin so the compiler's own bookkeeping sees it.
+  auto dma_wait = []() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  float sl = 0.f, sdl = 0.f;
+  auto gload = [&](int t, int slot) __attribute__((always_inline)) {
+    const uint8_t* s = smem + slot * SLOT;
+    dma(Qh, s, CR, offr, t);
+    dma(Qh, s + G::RT, CC, offc, t);
+    dma(dOh, s + G::RT + G::CT, CR, offr, t);
+    dma(dOh, s + 2 * G::RT + G::CT, CC, offc, t);
     if (tid < kTile) {
       const int q = t * kTile + tid;
       const float l = q < N ? lseh[q] : kNegInf;
@@ -328,16 +385,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
       sdl = q < N ? delh[q] : 0.f;
     }
   };
-  auto lstore = [&](int slot) {
+  auto lstore = [&](int slot) __attribute__((always_inline)) {
     uint8_t* s = smem + slot * SLOT;
-#pragma unroll
-    for (int i = 0; i < G::SPT; ++i) {
-      const int id = tid + kThreadsB * i, r = id / G::CPR, col = id % G::CPR;
-      *reinterpret_cast<u32x4_t*>(s + r * G::RS + col * 16) = sq[i];
-      *reinterpret_cast<u32x4_t*>(s + G::RT + r * G::CS + col * 16) = sq[i];
-      *reinterpret_cast<u32x4_t*>(s + G::RT + G::CT + r * G::RS + col * 16) = sd[i];
-      *reinterpret_cast<u32x4_t*>(s + 2 * G::RT + G::CT + r * G::CS + col * 16) = sd[i];
-    }
     if (tid < kTile) {
       float* f = reinterpret_cast<float*>(s + 2 * G::RT + 2 * G::CT);
       f[tid] = sl;
@@ -346,7 +395,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
   };
   const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
 
-  auto step = [&](int g, const uint8_t* s) {
+  auto step = [&](int g, const uint8_t* s) __attribute__((always_inline)) {
     const int b = (g & 1) * 32;
     const uint8_t* qr = s + b * G::RS + roff;
     const uint8_t* qt = s + G::RT + b * G::CS + toff;
@@ -359,34 +408,34 @@ __global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
       st = mfma(frag_row(qr, c2), as_bf16x8(kf[c2]), st);
       dp = mfma(frag_row(dr, c2), as_bf16x8(vf[c2]), dp);
     }
-    // Registers 8 cc + i hold query 32 g + 16 cc + 8 half + i.
-    f32x4_t l2[4], d2[4];
+    // Registers 8 cc + 4 h4 + k hold query 32 g + 16 cc + 8 half + 4 h4 + k: each group
+    // of four reads its four lse and Delta values just before use.
+    const bool masked = (32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32);
+    uint32_t pk[8], dsk[8];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int h4 = 0; h4 < 2; ++h4) {
-        l2[2 * cc + h4] = *reinterpret_cast<const f32x4_t*>(fl + 16 * cc + 8 * half + 4 * h4);
-        d2[2 * cc + h4] = *reinterpret_cast<const f32x4_t*>(fl + kTile + 16 * cc + 8 * half + 4 * h4);
-      }
-    const bool masked = (32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32);
-    uint32_t pk[8], dsk[8];
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(fl + 16 * cc + 8 * half + 4 * h4);
+        const f32x4_t d4 =
+            *reinterpret_cast<const f32x4_t*>(fl + kTile + 16 * cc + 8 * half + 4 * h4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float sv[2], pv[2], dv2[2];
+        for (int k2 = 0; k2 < 4; k2 += 2) {
+          float pv[2], dv2[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = 2 * i + e;             // register r = 8 cc + j
-        const int cc = r >> 3, j = r & 7;
-        const float lq = l2[2 * cc + (j >> 2)][j & 3], dq = d2[2 * cc + (j >> 2)][j & 3];
-        const int q = 32 * g + 16 * cc + 8 * half + j;
-        sv[e] = st[r];
-        if (masked && (q >= N || (CAUSAL && krow > q))) sv[e] = kNegInf;
-        pv[e] = exp2_hw(fmaf(sv[e], c, -lq));
-        dv2[e] = pv[e] * (dp[r] - dq);
+          for (int e = 0; e < 2; ++e) {
+            const int k = k2 + e, r = 8 * cc + 4 * h4 + k;
+            const int q = 32 * g + 16 * cc + 8 * half + 4 * h4 + k;
+            float sv = st[r];
+            if (masked && (q >= N || (CAUSAL && krow > q))) sv = kNegInf;
+            pv[e] = exp2_hw(fmaf(sv, c, -l4[k]));
+            dv2[e] = pv[e] * (dp[r] - d4[k]);
+          }
+          const int i = (8 * cc + 4 * h4 + k2) >> 1;
+          pk[i] = pack_bf16x2(pv[0], pv[1]);
+          dsk[i] = pack_bf16x2(dv2[0], dv2[1]);
+        }
       }
-      pk[i] = pack_bf16x2(pv[0], pv[1]);
-      dsk[i] = pack_bf16x2(dv2[0], dv2[1]);
-    }
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const u32x4_t bp = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
@@ -401,18 +450,23 @@ __global__ __launch_bounds__(kThreadsB, 1) void dkdv_kernel(
 
   const int ntiles = k0 >= N ? 0 : ntiles_all - t_first;
   if (ntiles > 0) {
-    gload(t_first);
+    gload(t_first, 0);
     lstore(0);
   }
+  dma_wait();
   __syncthreads();
+  // Tile i is read from slot i & 1; the loads of tile i + 1 go to the other slot, which
+  // was last read before the barrier that ended tile i - 1, and are waited for before
+  // the barrier that ends tile i.
 #pragma unroll 1
   for (int i = 0; i < ntiles; ++i) {
     const int t = t_first + i;
-    if (i + 1 < ntiles) gload(t + 1);
+    if (i + 1 < ntiles) gload(t + 1, (i + 1) & 1);
     const uint8_t* s = smem + (i & 1) * SLOT;
     if (2 * t >= gs && 2 * t < nblk_all) step(2 * t, s);
     if (2 * t + 1 >= gs && 2 * t + 1 < nblk_all) step(2 * t + 1, s);
-    if (i + 1 < ntiles) lstore((i + 1) & 1);  // slot read during tile t-1, before its barrier
+    if (i + 1 < ntiles) lstore((i + 1) & 1);
+    dma_wait();
     __syncthreads();
   }
 
@@ -443,7 +497,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t s) {
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
   const int64_t dblocks = (rows + 15) / 16;
-  const int nt = (a.N + kRowsB - 1) / kRowsB, ntq = (a.N + kRowsQ - 1) / kRowsQ;
+  const int nt = (a.N + KV<D>::kRows - 1) / KV<D>::kRows, ntq = (a.N + kRowsQ - 1) / kRowsQ;
   const int64_t blocks = int64_t(BH) * nt, qblocks = int64_t(BH) * ntq;
   if (dblocks > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((delta_kernel<D>), dim3(unsigned(dblocks)), dim3(256), 0, s, dout, a.o,
@@ -454,7 +508,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t s) {
                      k, v, dout, a.lse, a.delta, a.dq, a.N, BH, ntq, c, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreadsB), 0, s, q,
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(KV<D>::kThreads), 0, s, q,
                      k, v, dout, a.lse, a.delta, a.dk, a.dv, a.N, BH, nt, c, a.scale);
   return hipGetLastError();
 }
