@@ -7,8 +7,8 @@
 //
 // decode_partials is a pure stream over K and V (about one flop per byte), so it is
 // laid out for HBM: one workgroup per (head, chunk), four wavefronts each taking
-// 8*R keys per step with 16-byte loads that tile whole key rows (R rows per
-// wave-wide load), K and V requests issued together, dot products finished with
+// 16*R keys per step with non-temporal 16-byte loads that tile whole key rows (R rows
+// per wave-wide load), K and V requests issued together, dot products finished with
 // cross-lane adds inside a row, and the four wavefronts' states merged in LDS.
 #include "device.h"
 #include "launch.h"
@@ -17,7 +17,7 @@ namespace fa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kLoads = 8;  // 16-byte loads per lane per step, per tensor
+constexpr int kLoads = 16;  // 16-byte loads per lane per step, per tensor
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(64 * kWaves) void decode_partials_kernel(
@@ -55,8 +55,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partials_kernel(
     for (int i = 0; i < kLoads; ++i) {
       const int key = jb + i * RPW + row;
       const bool ok = key < j1;
-      kr[i] = ok ? load16(Kh + int64_t(key) * rowbytes) : u32x4_t{0, 0, 0, 0};
-      vr[i] = ok ? load16(Vh + int64_t(key) * rowbytes) : u32x4_t{0, 0, 0, 0};
+      // Non-temporal: K and V are read once, so nothing is kept in the caches.
+      kr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kh + int64_t(key) * rowbytes))
+                 : u32x4_t{0, 0, 0, 0};
+      vr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vh + int64_t(key) * rowbytes))
+                 : u32x4_t{0, 0, 0, 0};
     }
     float s[kLoads];
     float mx = kNegInf;
