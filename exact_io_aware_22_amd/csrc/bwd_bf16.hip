@@ -28,10 +28,10 @@
 // column-wise (transposing reads) is stored twice in LDS, with +16-byte rows for the
 // former and +64-byte rows for the latter: each padding keeps its own read pattern
 // free of bank conflicts on 64 banks, and no single padding serves both.
-// Staging: dq_kernel (8 wavefronts, 256 query rows) stages K and V through registers
-// into two LDS slots; dkdv_kernel (8 wavefronts at D = 64, 4 at D = 128) stages Q and
-// dO by direct global -> LDS loads, each into both of its layouts, so no registers
-// hold staged data. One barrier per 64-row tile in both.
+// Staging: both kernels load their 64-row tiles by direct global -> LDS loads, each
+// tile into every layout it is read in, so no registers hold staged data (dq_kernel:
+// K and V, 8 wavefronts, 256 query rows; dkdv_kernel: Q and dO, 8 wavefronts at D = 64,
+// 4 at D = 128). Two LDS slots, one barrier per tile.
 #include "device.h"
 #include "launch.h"
 
@@ -97,6 +97,45 @@ __device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* base, int cc, int db,
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+// Direct global -> LDS staging of one 64-row tile (global_load_lds_dwordx4, as in the
+// forward kernel) into a padded layout of C kilobytes (row stride 16 C bytes): one load
+// moves 64 lanes x 16 bytes to 1 KB of consecutive LDS at M0 + 16 lane, so lane i of
+// kilobyte j fills chunk 64 j + i of the padded tile, i.e. row (64 j + i) / C and column
+// (64 j + i) % C; pad columns take a copy of column CPR - 1 and are never read. Rows
+// past N - 1 take row N - 1 (finite; masked by the caller). Wavefront w issues
+// kilobytes w, w + WAVES, ... The loads are issued from inline assembly so that the
+// compiler, which does not see them write LDS, adds no waits before later LDS reads;
+// callers wait for them (vmcnt) before the barrier that publishes the tile. The
+// compiler makes no use of M0 in these kernels, which the assembly sets per load.
+template <int D, int C, int WAVES>
+__device__ __forceinline__ void dma_tile(const uint16_t* src, const uint8_t* region, int t,
+                                         int N, int wave, int lane) {
+  constexpr int CPR = D / 8, MAXI = (C + WAVES - 1) / WAVES;
+  constexpr int kRowShift = __builtin_ctz(2 * D);
+  const uint64_t b64 = reinterpret_cast<uint64_t>(src) + uint64_t(t) * kTile * D * 2;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(
+      uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64))))) |
+      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
+  const bool ragged = t * kTile + kTile > N;
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(const uint8_t, region)));
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int j = wave + WAVES * i;
+    if (j < C) {
+      const int p = 64 * j + lane, r = p / C, col = min(p % C, CPR - 1);
+      const int row = ragged ? min(t * kTile + r, N - 1) - t * kTile : r;
+      const uint32_t off = uint32_t(row << kRowShift) + uint32_t(col * 16);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(m0), "v"(off), "s"(base)
+                   : "memory");
+    }
+  }
+}
+// s_waitcnt vmcnt(0), through the builtin so the compiler's own bookkeeping sees it.
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup -> (head, tile): all tiles of a head on one XCD, heaviest first.
 // heavy_last_tile: causal dq (the last query tiles see the most keys); otherwise causal
@@ -187,26 +226,14 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
 
   // Staging: chunk i of a thread is row (tid + 256 i) / CPR, column (tid + 256 i) % CPR
   // of the 64-key tile; rows past the end read the last row (finite; masked below).
-  constexpr int SPQ = kTile * G::CPR / kThreadsQ;  // 16-byte chunks per thread per tile
-  u32x4_t sk[SPQ], sv[SPQ];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < SPQ; ++i) {
-      const int id = tid + kThreadsQ * i, r = id / G::CPR, col = id % G::CPR;
-      const int64_t gr = min(t * kTile + r, N - 1);
-      sk[i] = load16(Kh + gr * D + col * 8);
-      sv[i] = load16(Vh + gr * D + col * 8);
-    }
-  };
-  auto lstore = [&](int slot) {
-    uint8_t* s = smem + slot * SLOT;
-#pragma unroll
-    for (int i = 0; i < SPQ; ++i) {
-      const int id = tid + kThreadsQ * i, r = id / G::CPR, col = id % G::CPR;
-      *reinterpret_cast<u32x4_t*>(s + r * G::RS + col * 16) = sk[i];
-      *reinterpret_cast<u32x4_t*>(s + G::RT + r * G::CS + col * 16) = sk[i];
-      *reinterpret_cast<u32x4_t*>(s + G::RT + G::CT + r * G::RS + col * 16) = sv[i];
-    }
+  // K (into its row and transposing layouts) and V (row layout) by direct loads.
+  constexpr int CR = G::RS / 16, CC = G::CS / 16;
+  static_assert(G::RT == CR * 1024 && G::CT == CC * 1024, "a padded tile is C kilobytes");
+  auto gload = [&](int t, int slot) __attribute__((always_inline)) {
+    const uint8_t* s = smem + slot * SLOT;
+    dma_tile<D, CR, kWavesQ>(Kh, s, t, N, wave, lane);
+    dma_tile<D, CC, kWavesQ>(Kh, s + G::RT, t, N, wave, lane);
+    dma_tile<D, CR, kWavesQ>(Vh, s + G::RT + G::CT, t, N, wave, lane);
   };
   const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
   const int first_masked = CAUSAL ? min(N >> 5, qw0 >> 5) : (N >> 5);
@@ -245,18 +272,19 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
     }
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (ntiles > 0) gload(0, 0);
+  dma_wait();
   __syncthreads();
+  // Tile t is read from slot t & 1; the loads of tile t + 1 go to the other slot, last
+  // read before the barrier that ended tile t - 1, and are waited for before the
+  // barrier that ends tile t.
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < ntiles) gload(t + 1, (t + 1) & 1);
     const uint8_t* s = smem + (t & 1) * SLOT;
     if (2 * t < nblk) step(2 * t, s);
     if (2 * t + 1 < nblk) step(2 * t + 1, s);
-    if (t + 1 < ntiles) lstore((t + 1) & 1);  // slot read during tile t-1, before its barrier
+    dma_wait();
     __syncthreads();
   }
 
@@ -322,62 +350,17 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
     dka[db] = f32x16_t{};
   }
 
-  // Q and dO tiles reach LDS by direct global -> LDS loads (global_load_lds_dwordx4,
-  // as in the forward kernel), each into both of its layouts: one load moves 64 lanes x
-  // 16 bytes to 1 KB of consecutive LDS at M0 + 16 lane, and a padded tile is exactly
-  // CR (row layout) or CC (transposing layout) such kilobytes, so lane i of kilobyte j
-  // fills chunk 64 j + i, i.e. row (64 j + i) / C and column (64 j + i) % C; pad columns
-  // take a copy of column CPR - 1 and are never read. In a ragged tile, rows past the
-  // end take row N - 1 (finite; masked). Wavefront w issues kilobytes w, w + 8, w + 16.
-  // The 64 lse and Delta values of a tile go through registers (threads 0..63).
+  // Q and dO by direct loads, each into its row and transposing layouts; the 64 lse
+  // and Delta values of a tile go through registers (threads 0..63).
   constexpr int CR = G::RS / 16, CC = G::CS / 16;
-  constexpr int MAXI = (CC + kWavesB - 1) / kWavesB;
   static_assert(G::RT == CR * 1024 && G::CT == CC * 1024, "a padded tile is C kilobytes");
-  auto chunk_off = [&](int j, int C) -> uint32_t __attribute__((always_inline)) {
-    const int p = 64 * j + lane, r = p / C, col = min(p % C, G::CPR - 1);
-    return uint32_t(r * D * 2 + col * 16);
-  };
-  uint32_t offr[MAXI], offc[MAXI];
-#pragma unroll
-  for (int i = 0; i < MAXI; ++i) {
-    offr[i] = chunk_off(wave + kWavesB * i, CR);
-    offc[i] = chunk_off(wave + kWavesB * i, CC);
-  }
-  auto dma = [&](const uint16_t* src, const uint8_t* region, int C, const uint32_t (&d)[MAXI],
-                 int t) __attribute__((always_inline)) {
-    const uint64_t b64 = reinterpret_cast<uint64_t>(src) + uint64_t(t) * kTile * D * 2;
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(
-        uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64))))) |
-        (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
-    const bool ragged = t * kTile + kTile > N;
-    const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(const uint8_t, region)));
-    constexpr int kRowShift = __builtin_ctz(2 * D);
-#pragma unroll
-    for (int i = 0; i < MAXI; ++i) {
-      const int j = wave + kWavesB * i;
-      if (j < C) {
-        uint32_t off = d[i];
-        if (ragged) {  // redirect rows past N - 1 to row N - 1
-          const int r = int(off >> kRowShift);
-          off -= uint32_t((r - (min(t * kTile + r, N - 1) - t * kTile)) << kRowShift);
-        }
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                     :
-                     : "s"(m0), "v"(off), "s"(base)
-                     : "memory");
-      }
-    }
-  };
-  // s_waitcnt vmcnt(0), through the builtin so the compiler's own bookkeeping sees it.
-  auto dma_wait = []() { __builtin_amdgcn_s_waitcnt(0x0F70); };
   float sl = 0.f, sdl = 0.f;
   auto gload = [&](int t, int slot) __attribute__((always_inline)) {
     const uint8_t* s = smem + slot * SLOT;
-    dma(Qh, s, CR, offr, t);
-    dma(Qh, s + G::RT, CC, offc, t);
-    dma(dOh, s + G::RT + G::CT, CR, offr, t);
-    dma(dOh, s + 2 * G::RT + G::CT, CC, offc, t);
+    dma_tile<D, CR, kWavesB>(Qh, s, t, N, wave, lane);
+    dma_tile<D, CC, kWavesB>(Qh, s + G::RT, t, N, wave, lane);
+    dma_tile<D, CR, kWavesB>(dOh, s + G::RT + G::CT, t, N, wave, lane);
+    dma_tile<D, CC, kWavesB>(dOh, s + 2 * G::RT + G::CT, t, N, wave, lane);
     if (tid < kTile) {
       const int q = t * kTile + tid;
       const float l = q < N ? lseh[q] : kNegInf;
