@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "decode_partials_kernel": "exact_io_aware_22_amd/csrc/decode.hip",
     "row_reduce_kernel<SoftmaxMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
     "row_reduce_kernel<WelfordMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
+    "delta_kernel + dq_kernel + dkdv_kernel": "exact_io_aware_22_amd/csrc/bwd_bf16.hip",
 }
 
 
@@ -254,7 +255,9 @@ def bench_backward(steps: int, warmup: int, torch, fa, make_inputs, W, check: bo
            "flop_convention": "2.5 x forward (5 products), halved for causal",
            "roofline": {"kernels": "delta_kernel + dq_kernel + dkdv_kernel", "bound": "mfma",
                         "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                        "frac": achieved / PEAK_BF16_TFLOPS,
+                        "traffic": measured_traffic("delta_kernel + dq_kernel + dkdv_kernel",
+                                                    HEADLINE),
                         "algorithmic_flops_per_launch": flops}}
     if check:
         import oracle
