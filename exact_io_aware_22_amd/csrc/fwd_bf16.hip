@@ -466,18 +466,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // ---- read out: o / d once, lse = ln(sum) = (r c + log2 d) ln 2
   const float dl = halves_sum(d_lse), dq = halves_sum(d_out);
   const int qi = qw0 + l32;
-  if (qi < N) {
+  // O leaves through LDS so that every global store writes whole row pieces: each
+  // wavefront stages its 32 rows x W head dims (normalised) in its own LDS region (the
+  // rings are idle after the last barrier, and every direct load has been waited for),
+  // then reads them back row-contiguous; W = 64 (D = 128) or 32 (D = 64), D / W passes.
+  {
     const float inv = dq > 0.f ? 1.f / dq : 0.f;
-    float* orow = O + head + int64_t(qi) * D;
+    constexpr int W = D == 128 ? 64 : 32, CH = W / 4, RPI = 64 / CH;
+    constexpr int OS = W * 4 + 16;  // bytes per staged row (+16: 16 rows on distinct banks)
+    static_assert(kWaves * 32 * OS <= G::LDS, "output staging fits the rings");
+    uint8_t* const ost = smem + wave * (32 * OS);
 #pragma unroll
-    for (int db = 0; db < G::NDB; ++db)
+    for (int pass = 0; pass < D / W; ++pass) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4_t val = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
-                             oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
-        *reinterpret_cast<f32x4_t*>(orow + 32 * db + 8 * g4 + 4 * half) = val;
+      for (int dbp = 0; dbp < W / 32; ++dbp) {
+        const int db = pass * (W / 32) + dbp;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4_t val = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv,
+                               oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv};
+          *reinterpret_cast<f32x4_t*>(ost + l32 * OS + (32 * dbp + 8 * g4 + 4 * half) * 4) = val;
+        }
       }
-    if (half == 0)
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = RPI * i + lane / CH, ch = lane % CH;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ost + r * OS + ch * 16);
+        if (qw0 + r < N)
+          *reinterpret_cast<f32x4_t*>(O + head + int64_t(qw0 + r) * D + pass * W + ch * 4) = v;
+      }
+    }
+    if (qi < N && half == 0)
       LSE[row0 + qi] = dl > 0.f ? (m_ref * c + log2_hw(dl)) * kLn2 : kNegInf;
   }
 }
