@@ -44,7 +44,8 @@
 //     of bank conflicts on 64 LDS banks; slot offsets are uniform scalars rotated
 //     once per tile, so every fragment address is one per-lane base plus a constant.
 //   * Tiles where nothing is masked, ragged or final run in a loop of their own with
-//     no branches but the rare rescale; the remaining tiles take the general loop.
+//     no branches but the rare rescale; the remaining tiles take the general body,
+//     which the steady loop is nested in (one copy of each).
 //   * The V^T operand of the PV MFMA is read with the transposing LDS read
 //     ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 //     (i mod 4) of what lane 4e + i/4 addressed, for e = 0..3, so lanes that address
@@ -53,6 +54,12 @@
 //   * Causal: a wavefront stops at its diagonal block, which is the only block it
 //     masks (plus the ragged tail); heaviest query tiles launch first and all tiles
 //     of a head go to one XCD so its K/V stream is shared in that XCD's L2.
+//   * Sliding windows and packed sequences use the same loop: a wavefront folds only
+//     the blocks its rows' windows reach, the workgroup stages only the tiles they
+//     cover, and blocks that straddle a window edge are masked. A packed unit is one
+//     (sequence, head) pair with its own row count and first row.
+//   * O is normalised in registers and leaves through LDS (each wavefront's 32 rows
+//     staged and read back row-contiguous), so every store writes whole row pieces.
 #include "device.h"
 #include "launch.h"
 
