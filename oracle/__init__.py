@@ -19,4 +19,11 @@ from .fp64 import (  # noqa: F401
 )
 from .backward import attention_backward  # noqa: F401,E402
 from .masks import attention_varlen, attention_window, visible  # noqa: F401,E402
-from .monoids import log_sum_exp, moments, softmax_stats, variance  # noqa: F401,E402
+from .monoids import (  # noqa: F401,E402
+    log_sum_exp,
+    moments,
+    moments_scan,
+    softmax_stats,
+    softmax_stats_scan,
+    variance,
+)

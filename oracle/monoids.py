@@ -17,9 +17,9 @@ Sources ("Learning FlashAttention the Hard Way -- Part 1", cloudrift.ai):
   and the identity (0, 0, 0); the variance M2 / n (population) or M2 / (n - 1)
   (sample) read off the final triple (section "The Same Move: Welford's Variance").
 
-`softmax_stats` and `moments` are the definitions, evaluated directly (max, then the
-sum of shifted exponentials; mean, then the sum of squared deviations), a whole row at
-a time. The inject / combine functions are the monoid steps in the pages' notation, for
+`softmax_stats` and `moments` (and their prefix scans) are the definitions, evaluated
+directly (max, then the sum of shifted exponentials; mean, then the sum of squared
+deviations), a whole row (or prefix) at a time. The inject / combine functions are the monoid steps in the pages' notation, for
 tests that fold them in arbitrary brackets and check the fold against the definitions.
 
 The pages print the merges' formulas only as images; the readings taken are the
@@ -86,6 +86,38 @@ def variance(x, ddof: int = 0):
     """M2 / (n - ddof) per row: population variance (ddof 0) or sample variance (1)."""
     count, _, m2 = moments(x)
     return m2 / (count - ddof)
+
+
+# --------------------------------------------------------------------------- prefix scans
+# A prefix sum is one more re-bracketing that any monoid allows (section "Wrap-Up",
+# first point): the inclusive scan of a row is, at every position j, the reduction of
+# elements 0..j. These are that definition, each prefix reduced from scratch (O(n^2)
+# per row, for test sizes).
+def softmax_stats_scan(x):
+    """Per row of x [rows, n] and position j: m[r, j] = max_{i<=j} x[r, i] and
+    d[r, j] = sum_{i<=j} e^{x[r, i] - m[r, j]}; a prefix of only -inf is (-inf, 0).
+    Returns (m, d), each [rows, n] float64."""
+    x = _f64(x)
+    rows, n = x.shape
+    m = np.full((rows, n), NEG_INF)
+    d = np.zeros((rows, n))
+    for j in range(n):
+        mj, dj = softmax_stats(x[:, :j + 1])
+        m[:, j], d[:, j] = mj, dj
+    return m, d
+
+
+def moments_scan(x):
+    """Per row of x [rows, n] and position j: the mean and M2 of x[r, 0..j] (count
+    j + 1). Returns (mean, m2), each [rows, n] float64."""
+    x = _f64(x)
+    rows, n = x.shape
+    mean = np.zeros((rows, n))
+    m2 = np.zeros((rows, n))
+    for j in range(n):
+        _, mu, q = moments(x[:, :j + 1])
+        mean[:, j], m2[:, j] = mu, q
+    return mean, m2
 
 
 # --------------------------------------------------------------------------- monoid steps

@@ -10,6 +10,9 @@ None of these reuses the oracle's formulas:
   -inf entries (the identity) and empty rows;
 * the pages' monoid claim: folding the injections with the combine in random
   bracketings and orders gives the definition;
+* prefix scans: the last position equals the (pinned) reduction, closed forms per
+  prefix (1..j, constant and geometric rows, -inf prefixes), exact rational moments of
+  every prefix, and a Blelloch up-sweep / down-sweep scan built from the monoid steps;
 * planted mistakes, each of which must fail at least one pin.
 """
 import math
@@ -239,3 +242,110 @@ def test_planted_softmax_combine_mistakes_fail(combine):
 def test_planted_welford_combine_mistakes_fail(combine):
     with pytest.raises(AssertionError):
         pin_welford_fold(om.moments, combine=combine)
+
+
+# ------------------------------------------------------------------ prefix scans
+def pin_scan_last_is_reduction(scan_sm, scan_mo):
+    x = RNG.standard_normal((4, 57)) * 7
+    m, d = scan_sm(x)
+    mr, dr = om.softmax_stats(x)
+    assert np.array_equal(m[:, -1], mr) and np.allclose(d[:, -1], dr, rtol=1e-13)
+    mean, m2 = scan_mo(x)
+    _, mu, q = om.moments(x)
+    assert np.allclose(mean[:, -1], mu, rtol=1e-14) and np.allclose(m2[:, -1], q, rtol=1e-12)
+
+
+def pin_scan_closed_forms(scan_sm, scan_mo):
+    k = 60
+    j = np.arange(k)
+    mean, m2 = scan_mo(np.arange(1, k + 1, dtype=float)[None])
+    assert np.array_equal(mean[0], (j + 2) / 2)               # mean of 1..j+1
+    assert np.allclose(m2[0], (j + 1) * ((j + 1) ** 2 - 1) / 12, rtol=1e-13, atol=0)
+    m, d = scan_sm(np.full((1, k), -2.0))
+    assert np.all(m == -2.0) and np.array_equal(d[0], j + 1.0)  # constant: d counts
+    m, d = scan_sm((j * math.log(2.0))[None])                   # x_j = j ln 2, rising
+    assert np.allclose(m[0], j * math.log(2.0), rtol=1e-15)
+    assert np.allclose(d[0], 2.0 - 2.0 ** (-j), rtol=1e-13)   # sum_i 2^{i-j}
+    m, d = scan_sm(np.array([[-math.inf, -math.inf, 1.0, -math.inf]]))
+    assert list(m[0]) == [-math.inf, -math.inf, 1.0, 1.0] and list(d[0]) == [0.0, 0.0, 1.0, 1.0]
+
+
+def pin_scan_exact_moments(scan_mo):
+    x = np.round(RNG.standard_normal((2, 20)) * 16) / 4
+    mean, m2 = scan_mo(x)
+    for r in range(2):
+        for j in range(20):
+            emu, em2 = _exact_moments(x[r, :j + 1])
+            assert abs(mean[r, j] - float(emu)) <= 1e-15 * max(1.0, abs(float(emu)))
+            assert abs(m2[r, j] - float(em2)) <= 1e-13 * max(1.0, float(em2))
+
+
+def _blelloch(items, inject, combine, identity):
+    """Exclusive scan by the up-sweep / down-sweep of a balanced tree (Blelloch), then
+    one more combine per element: a bracketing unlike the left fold of the definition."""
+    n = 1
+    while n < len(items):
+        n *= 2
+    a = [inject(v) for v in items] + [identity()] * (n - len(items))
+    tree = list(a)
+    step = 1
+    while step < n:  # up-sweep
+        for i in range(2 * step - 1, n, 2 * step):
+            tree[i] = combine(tree[i - step], tree[i])
+        step *= 2
+    tree[n - 1] = identity()
+    step = n // 2
+    while step >= 1:  # down-sweep
+        for i in range(2 * step - 1, n, 2 * step):
+            left = tree[i - step]
+            tree[i - step] = tree[i]
+            tree[i] = combine(tree[i], left)
+        step //= 2
+    return [combine(tree[i], a[i]) for i in range(len(items))]
+
+
+def pin_scan_blelloch(scan_sm, scan_mo):
+    x = RNG.standard_normal(45) * 9
+    m, d = scan_sm(x[None])
+    st = _blelloch(list(x), om.softmax_inject, om.softmax_combine, om.softmax_identity)
+    assert [s[0] for s in st] == list(m[0])
+    assert np.allclose([s[1] for s in st], d[0], rtol=1e-12)
+    mean, m2 = scan_mo(x[None] + 3)
+    st = _blelloch(list(x + 3), om.welford_inject, om.welford_combine, om.welford_identity)
+    assert np.allclose([s[1] for s in st], mean[0], rtol=1e-13)
+    assert np.allclose([s[2] for s in st], m2[0], rtol=1e-11, atol=1e-12)
+
+
+def test_scan_pins():
+    pin_scan_last_is_reduction(om.softmax_stats_scan, om.moments_scan)
+    pin_scan_closed_forms(om.softmax_stats_scan, om.moments_scan)
+    pin_scan_exact_moments(om.moments_scan)
+    pin_scan_blelloch(om.softmax_stats_scan, om.moments_scan)
+
+
+def _exclusive_softmax_scan(x):  # planted: position j reduces 0..j-1
+    m, d = om.softmax_stats_scan(x)
+    x = np.asarray(x, dtype=float)
+    m2 = np.concatenate([np.full((x.shape[0], 1), -math.inf), m[:, :-1]], axis=1)
+    d2 = np.concatenate([np.zeros((x.shape[0], 1)), d[:, :-1]], axis=1)
+    return m2, d2
+
+
+def _running_max_only(x):  # planted: d not rescaled when the maximum moves
+    x = np.asarray(x, dtype=float)
+    m = np.maximum.accumulate(x, axis=1)
+    d = np.cumsum(np.exp(x - m), axis=1)
+    return m, d
+
+
+@pytest.mark.parametrize("impl", [_exclusive_softmax_scan, _running_max_only])
+def test_planted_scan_mistakes_fail(impl):
+    failed = False
+    for pin in (lambda: pin_scan_last_is_reduction(impl, om.moments_scan),
+                lambda: pin_scan_closed_forms(impl, om.moments_scan),
+                lambda: pin_scan_blelloch(impl, om.moments_scan)):
+        try:
+            pin()
+        except AssertionError:
+            failed = True
+    assert failed
