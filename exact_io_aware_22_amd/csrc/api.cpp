@@ -163,3 +163,34 @@ int fa_moments(const void* x, float* mean, float* m2, int rows, int n, int dtype
 }
 
 }  // extern "C"
+
+namespace {
+
+// Shared validation of the two prefix scans: x [rows][n] of dtype; out0, out1 [rows][n].
+int row_scan(const void* x, float* out0, float* out1, int rows, int n, int dtype, void* stream,
+             hipError_t (*launch)(const fa::RowReduceArgs&, hipStream_t)) {
+  if (rows < 0 || n < 0 || !count_ok(rows, n, 2, 1)) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (rows == 0 || n == 0) return FA_OK;  // empty: no pointer is touched
+  if (!x || !out0 || !out1) return FA_ERR_NULL;
+  if (!aligned(x, dtype == FA_BF16 ? 2 : 4) || !aligned(out0, 4) || !aligned(out1, 4))
+    return FA_ERR_ALIGN;
+  fa::RowReduceArgs a{x, rows, n, dtype == FA_BF16, out0, out1};
+  return hip_status(launch(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_softmax_scan(const void* x, float* m, float* d, int rows, int n, int dtype,
+                    void* stream) {
+  return row_scan(x, m, d, rows, n, dtype, stream, fa::launch_softmax_scan);
+}
+
+int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int dtype,
+                    void* stream) {
+  return row_scan(x, mean, m2, rows, n, dtype, stream, fa::launch_moments_scan);
+}
+
+}  // extern "C"

@@ -63,7 +63,7 @@ struct RowReduceArgs {
   int64_t rows;
   int n;
   bool bf16;
-  float* out0;  // softmax: m; moments: mean
+  float* out0;  // softmax: m; moments: mean ([rows], or [rows][n] for a scan)
   float* out1;  // softmax: d; moments: M2
 };
 
@@ -76,5 +76,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_softmax_stats(const RowReduceArgs& a, hipStream_t s);
 hipError_t launch_moments(const RowReduceArgs& a, hipStream_t s);
+// Inclusive scans: out0, out1 are [rows][n].
+hipError_t launch_softmax_scan(const RowReduceArgs& a, hipStream_t s);
+hipError_t launch_moments_scan(const RowReduceArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -67,10 +67,15 @@ struct SoftmaxMonoid {
   __device__ static S shfl_xor(S s, int mask) {
     return {__shfl_xor(s.m, mask), __shfl_xor(s.d, mask)};
   }
+  __device__ static S shfl_up(S s, int delta) {
+    return {__shfl_up(s.m, delta), __shfl_up(s.d, delta)};
+  }
   __device__ static void store(S s, float* out0, float* out1, int64_t row) {
     out0[row] = s.m;
     out1[row] = s.d;
   }
+  __device__ static float first(S s) { return s.m; }
+  __device__ static float second(S s) { return s.d; }
 };
 
 struct WelfordMonoid {
@@ -105,10 +110,15 @@ struct WelfordMonoid {
   __device__ static S shfl_xor(S s, int mask) {
     return {__shfl_xor(s.n, mask), __shfl_xor(s.mu, mask), __shfl_xor(s.m2, mask)};
   }
+  __device__ static S shfl_up(S s, int delta) {
+    return {__shfl_up(s.n, delta), __shfl_up(s.mu, delta), __shfl_up(s.m2, delta)};
+  }
   __device__ static void store(S s, float* out0, float* out1, int64_t row) {
     out0[row] = s.mu;
     out1[row] = s.m2;
   }
+  __device__ static float first(S s) { return s.mu; }
+  __device__ static float second(S s) { return s.m2; }
 };
 
 // ---------------------------------------------------------------- element access
@@ -227,6 +237,114 @@ __global__ __launch_bounds__(256) void row_reduce_kernel(const T* __restrict__ x
   }
 }
 
+// ---------------------------------------------------------------- the prefix scan
+// Inclusive scan of every row: output j is the state of elements 0..j. A prefix scan is
+// one more re-bracketing any monoid allows (section "Wrap-Up", first point), here on
+// the same pieces: one 256-thread workgroup per row, the row in blocks of 256 x 8
+// elements. Thread t folds its 8 consecutive elements left to right (keeping each
+// partial state), the 256 thread totals are scanned (an inclusive scan across each
+// wavefront with shfl_up, then the four wavefront totals through LDS), and element i
+// of thread t is written as carry + (totals of threads before t) + (its own partial i);
+// the block's total joins the carry for the next block. ALIGNED: x and both outputs
+// start on 16-byte boundaries and rows are whole 16-byte multiples, so a thread's 8
+// elements are read and written with vector accesses.
+template <class M, typename T, bool ALIGNED>
+__global__ __launch_bounds__(256) void row_scan_kernel(const T* __restrict__ x, int n,
+                                                     float* __restrict__ out0,
+                                                     float* __restrict__ out1) {
+  using S = typename M::S;
+  __shared__ S wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const T* p = x + row * int64_t(n);
+  float* o0 = out0 + row * int64_t(n);
+  float* o1 = out1 + row * int64_t(n);
+  S carry = M::identity();
+  for (int base = 0; base < n; base += 256 * kK) {
+    const int e0 = base + kK * tid;
+    S st[kK];
+    S run = M::identity();
+    if (ALIGNED && e0 + kK <= n) {
+      float v[kK];
+#pragma unroll
+      for (int j = 0; j < kK / Elem<T>::kVec; ++j) {
+        float w[Elem<T>::kVec];
+        Elem<T>::vec(p + e0 + j * Elem<T>::kVec, w);
+#pragma unroll
+        for (int i = 0; i < Elem<T>::kVec; ++i) v[j * Elem<T>::kVec + i] = w[i];
+      }
+#pragma unroll
+      for (int i = 0; i < kK; ++i) {
+        run = M::combine(run, M::inject(v[i]));
+        st[i] = run;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kK; ++i) {
+        if (e0 + i < n) run = M::combine(run, M::inject(Elem<T>::scalar(p + e0 + i)));
+        st[i] = run;
+      }
+    }
+    // inclusive scan of the thread totals across the wavefront
+    S tot = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const S o = M::shfl_up(tot, off);
+      if (lane >= off) tot = M::combine(o, tot);
+    }
+    S excl = M::shfl_up(tot, 1);  // totals of the lanes before this one
+    if (lane == 0) excl = M::identity();
+    if (lane == 63) wtot[wave] = tot;
+    __syncthreads();
+    S pre = carry, blk = carry;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) pre = M::combine(pre, wtot[w]);
+      blk = M::combine(blk, wtot[w]);
+    }
+    pre = M::combine(pre, excl);
+    __syncthreads();  // wtot is rewritten by the next block
+    float r0[kK], r1[kK];
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+      const S r = M::combine(pre, st[i]);
+      r0[i] = M::first(r);
+      r1[i] = M::second(r);
+    }
+    if (ALIGNED && e0 + kK <= n) {
+#pragma unroll
+      for (int j = 0; j < kK; j += 4) {
+        *reinterpret_cast<f32x4_t*>(o0 + e0 + j) = f32x4_t{r0[j], r0[j + 1], r0[j + 2], r0[j + 3]};
+        *reinterpret_cast<f32x4_t*>(o1 + e0 + j) = f32x4_t{r1[j], r1[j + 1], r1[j + 2], r1[j + 3]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kK; ++i)
+        if (e0 + i < n) {
+          o0[e0 + i] = r0[i];
+          o1[e0 + i] = r1[i];
+        }
+    }
+    carry = blk;
+  }
+}
+
+template <class M, typename T>
+hipError_t launch_scan(const RowReduceArgs& a, hipStream_t st) {
+  if (a.rows > 0x7fffffff) return hipErrorInvalidValue;
+  const T* x = static_cast<const T*>(a.x);
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(a.out0) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(a.out1) & 15) == 0 && (a.n % kK) == 0;
+  if (aligned)
+    hipLaunchKernelGGL((row_scan_kernel<M, T, true>), dim3(unsigned(a.rows)), dim3(256), 0, st, x,
+                       a.n, a.out0, a.out1);
+  else
+    hipLaunchKernelGGL((row_scan_kernel<M, T, false>), dim3(unsigned(a.rows)), dim3(256), 0, st,
+                       x, a.n, a.out0, a.out1);
+  return hipGetLastError();
+}
+
 template <class M, typename T>
 hipError_t launch_rows(const RowReduceArgs& a, hipStream_t st) {
   // Four wavefronts share a row: measured faster than one wavefront per row on the
@@ -255,6 +373,14 @@ hipError_t launch_softmax_stats(const RowReduceArgs& a, hipStream_t s) {
 
 hipError_t launch_moments(const RowReduceArgs& a, hipStream_t s) {
   return a.bf16 ? launch_rows<WelfordMonoid, uint16_t>(a, s) : launch_rows<WelfordMonoid, float>(a, s);
+}
+
+hipError_t launch_softmax_scan(const RowReduceArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_scan<SoftmaxMonoid, uint16_t>(a, s) : launch_scan<SoftmaxMonoid, float>(a, s);
+}
+
+hipError_t launch_moments_scan(const RowReduceArgs& a, hipStream_t s) {
+  return a.bf16 ? launch_scan<WelfordMonoid, uint16_t>(a, s) : launch_scan<WelfordMonoid, float>(a, s);
 }
 
 }  // namespace fa

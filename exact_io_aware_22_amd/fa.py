@@ -24,7 +24,8 @@ _lib = None
 FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
-            "fa_backward", "fa_softmax_stats", "fa_moments", "fa_strerror", "fa_abi_version")
+            "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
+            "fa_strerror", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -50,6 +51,9 @@ def load():
     lib.fa_softmax_stats.restype = i
     lib.fa_moments.argtypes = [vp, vp, vp, i, i, i, vp]
     lib.fa_moments.restype = i
+    for name in ("fa_softmax_scan", "fa_moments_scan"):
+        getattr(lib, name).argtypes = [vp, vp, vp, i, i, i, vp]
+        getattr(lib, name).restype = i
     lib.fa_decode_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_decode_partials.restype = i
     lib.fa_combine_partials.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
@@ -185,6 +189,31 @@ def fa_moments(x, mean, m2, stream=None) -> None:
     _check(code, "fa_moments")
 
 
+def _scan_shapes(x, out0, out1):
+    _dense(x, out0, out1)
+    if x.dim() < 1:
+        raise ValueError("x needs at least one dimension (its rows are along the last)")
+    if out0.shape != x.shape or out1.shape != x.shape:
+        raise ValueError("scan outputs must have x's shape")
+    return math.prod(x.shape[:-1]), x.shape[-1]
+
+
+def fa_softmax_scan(x, m, d, stream=None) -> None:
+    """x: [..., n] (bf16 or fp32); m, d: fp32 of x's shape (inclusive prefix states)."""
+    rows, n = _scan_shapes(x, m, d)
+    code = load().fa_softmax_scan(_ptr(x), _ptr(m), _ptr(d), rows, n, _dtype_code(x),
+                                  _stream(stream))
+    _check(code, "fa_softmax_scan")
+
+
+def fa_moments_scan(x, mean, m2, stream=None) -> None:
+    """x: [..., n] (bf16 or fp32); mean, m2: fp32 of x's shape (inclusive prefix moments)."""
+    rows, n = _scan_shapes(x, mean, m2)
+    code = load().fa_moments_scan(_ptr(x), _ptr(mean), _ptr(m2), rows, n, _dtype_code(x),
+                                  _stream(stream))
+    _check(code, "fa_moments_scan")
+
+
 # ------------------------------------------------------------------ conveniences
 def softmax_stats(x, stream=None):
     """Allocate m, d (x's shape without its last dim, fp32) and run fa_softmax_stats."""
@@ -192,6 +221,22 @@ def softmax_stats(x, stream=None):
     d = torch.empty_like(m)
     fa_softmax_stats(x, m, d, stream)
     return m, d
+
+
+def softmax_scan(x, stream=None):
+    """Allocate m, d (x's shape, fp32) and run fa_softmax_scan."""
+    m = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    d = torch.empty_like(m)
+    fa_softmax_scan(x, m, d, stream)
+    return m, d
+
+
+def moments_scan(x, stream=None):
+    """Allocate mean, m2 (x's shape, fp32) and run fa_moments_scan."""
+    mean = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    m2 = torch.empty_like(mean)
+    fa_moments_scan(x, mean, m2, stream)
+    return mean, m2
 
 
 def moments(x, stream=None):

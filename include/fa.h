@@ -198,6 +198,23 @@ int fa_softmax_stats(const void* x, float* m, float* d, int rows, int n, int dty
  */
 int fa_moments(const void* x, float* mean, float* m2, int rows, int n, int dtype, void* stream);
 
+/*
+ * fa_softmax_scan, fa_moments_scan -- inclusive prefix scans of the same two monoids:
+ * a prefix sum is one more re-bracketing that any monoid allows (section "Wrap-Up",
+ * first point). For every row r and position j the state of x[r][0..j] is written:
+ *   fa_softmax_scan: m[r][j] = max_{i<=j} x[r][i], d[r][j] = sum_{i<=j} e^{x[r][i] - m[r][j]}
+ *                    (-inf, 0 while the prefix holds only -inf);
+ *   fa_moments_scan: mean[r][j] and m2[r][j] of the j + 1 elements x[r][0..j].
+ *   outputs : two [rows][n] float32 arrays, written.
+ * rows = 0 or n = 0 is an empty call (no pointer touched). Alignment: x to its element,
+ * outputs 4 bytes (16-byte aligned x and outputs with n a multiple of 8 take vector
+ * accesses). Element counts must fit int64 byte offsets (FA_ERR_SHAPE otherwise).
+ */
+int fa_softmax_scan(const void* x, float* m, float* d, int rows, int n, int dtype,
+                    void* stream);
+int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int dtype,
+                    void* stream);
+
 /* Static, human-readable name of an FA_* code (never NULL). */
 const char* fa_strerror(int code);
 

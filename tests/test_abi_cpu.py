@@ -36,7 +36,8 @@ def lib():
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
-         "fa_backward", "fa_softmax_stats", "fa_moments", "fa_strerror", "fa_abi_version"])
+         "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
+         "fa_strerror", "fa_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -190,3 +191,18 @@ def test_row_reduction_validation(lib, which):
     assert red(lib, which, o1=P + 2) == ALIGN
     assert red(lib, which, rows=0, x=None, o0=None, o1=None) == OK  # empty
     assert red(lib, which, rows=0, n=-1) == SHAPE                    # sizes first
+
+
+@pytest.mark.parametrize("which", ["fa_softmax_scan", "fa_moments_scan"])
+def test_row_scan_validation(lib, which):
+    assert red(lib, which, x=None) == NULL
+    assert red(lib, which, o1=None) == NULL
+    assert red(lib, which, rows=-1) == SHAPE
+    assert red(lib, which, n=-1) == SHAPE
+    assert red(lib, which, dtype=5) == DTYPE
+    assert red(lib, which, x=P + 1) == ALIGN
+    assert red(lib, which, x=P + 2, dtype=0) == ALIGN
+    assert red(lib, which, o0=P + 3) == ALIGN
+    assert red(lib, which, rows=0, x=None, o0=None, o1=None) == OK  # empty
+    assert red(lib, which, n=0, x=None, o0=None, o1=None) == OK     # empty rows
+    assert red(lib, which, rows=1 << 30, n=1 << 30) == SHAPE         # offsets overflow
