@@ -334,9 +334,11 @@ def bench_masks(steps: int, warmup: int, torch, fa, W, check: bool):
 
 
 def bench_reductions(steps: int, warmup: int, torch, fa, check: bool):
-    """fa_softmax_stats and fa_moments on their 1 GiB workloads: HBM-bound, so GB/s of
-    algorithmic bytes (every element read once, two float32 outputs per row written)
-    against 8 TB/s; with `check`, 64 seeded rows compared with the oracle."""
+    """fa_softmax_stats and fa_moments on their 1 GiB workloads, then the inclusive scans
+    (fa_softmax_scan, fa_moments_scan) of the same rows: HBM-bound, so GB/s of
+    algorithmic bytes (every element read once; two float32 outputs per row, or per
+    element for a scan, written) against 8 TB/s; with `check`, 64 seeded rows (18
+    sampled prefixes for a scan) compared with the oracle."""
     import numpy as np
 
     from exact_io_aware_22_amd.workloads import ROW_WORKLOADS, make_rows
@@ -376,7 +378,45 @@ def bench_reductions(steps: int, warmup: int, torch, fa, check: bool):
                 r["parity"] = {"rows": 64, "max_abs_err_mean": float(np.max(np.abs(ga - mu_ref))),
                                "max_rel_err_m2": float(np.max(np.abs(gb - m2_ref) / m2_ref))}
         res.append(r)
-        del x, xd, a, b
+        del a, b
+        # the inclusive scan of the same rows: every position's state written (two
+        # float32 outputs per element)
+        sa = torch.empty(w.rows, w.n, device="cuda")
+        sb = torch.empty(w.rows, w.n, device="cuda")
+        sfn = fa.fa_softmax_scan if softmax else fa.fa_moments_scan
+        ms = time_launches(lambda: sfn(xd, sa, sb), max(3, steps // 2), max(2, warmup // 2),
+                           torch)
+        nbytes = w.bytes_read() + 2 * 4 * w.rows * w.n
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        skernel = "row_scan_kernel<" + ("SoftmaxMonoid" if softmax else "WelfordMonoid") + ">"
+        rs = {"workload": name, "op": "inclusive scan", "ms": ms, "value": gbs, "unit": "GB/s",
+              "roofline": {"kernel": skernel, "bound": "hbm", "achieved": gbs,
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                           "traffic": None, "algorithmic_bytes_per_launch": nbytes}}
+        if check:
+            import oracle
+
+            # sampled (row, position) pairs: each prefix reduced by the oracle directly
+            rng = np.random.default_rng(6)
+            pairs = [(int(rng.integers(w.rows)), int(rng.integers(w.n))) for _ in range(16)]
+            pairs += [(0, 0), (w.rows - 1, w.n - 1)]
+            ga, gb = sa.cpu(), sb.cpu()
+            e0 = e1 = 0.0
+            for r_, j_ in pairs:
+                pref = x[r_:r_ + 1, :j_ + 1]
+                if softmax:
+                    m_ref, d_ref = oracle.softmax_stats(pref)
+                    e0 = max(e0, abs(float(ga[r_, j_]) - m_ref[0]))
+                    e1 = max(e1, abs(float(gb[r_, j_]) - d_ref[0]) / d_ref[0])
+                else:
+                    _, mu_ref, m2_ref = oracle.moments(pref)
+                    e0 = max(e0, abs(float(ga[r_, j_]) - mu_ref[0]))
+                    e1 = max(e1, abs(float(gb[r_, j_]) - m2_ref[0]) / max(m2_ref[0], 1e-30))
+            rs["parity"] = {"positions": len(pairs),
+                            ("max_abs_err_m" if softmax else "max_abs_err_mean"): e0,
+                            ("max_rel_err_d" if softmax else "max_rel_err_m2"): e1}
+        res.append(rs)
+        del x, xd, sa, sb
         torch.cuda.empty_cache()
     return res
 
