@@ -43,12 +43,14 @@ struct SoftmaxMonoid {
   };
   __device__ static S identity() { return {kNegInf, 0.f}; }
   __device__ static S inject(float x) { return x == kNegInf ? identity() : S{x, 1.f}; }
-  // Both sides rescaled to the larger maximum. A side at -inf contributes 2^-inf = 0;
-  // when both are -inf the exponents use 0 instead of m, so no -inf - (-inf) arises.
+  // Both sides rescaled to the larger maximum: the side that holds it keeps its d, the
+  // other is scaled by e^{(its m) - m}, one exponential per combine. A side at -inf
+  // contributes 2^-inf = 0; when both are -inf the factor is 0 and no -inf - (-inf)
+  // arises.
   __device__ static S combine(S a, S b) {
-    const float m = fmaxf(a.m, b.m);
-    const float mr = m == kNegInf ? 0.f : m;
-    return {m, a.d * exp2_hw((a.m - mr) * kLog2e) + b.d * exp2_hw((b.m - mr) * kLog2e)};
+    const float m = fmaxf(a.m, b.m), lo = fminf(a.m, b.m);
+    const float e = m == kNegInf ? 0.f : exp2_hw((lo - m) * kLog2e);
+    return {m, a.m >= b.m ? fmaf(b.d, e, a.d) : fmaf(a.d, e, b.d)};
   }
   // Merge the fold of K injections into s: the running maximum takes the block's
   // maximum, d is rescaled once to it, then the block's shifted exponentials add.
