@@ -43,6 +43,8 @@ KERNEL_SOURCES = {
     "decode_partials_kernel": "exact_io_aware_22_amd/csrc/decode.hip",
     "row_reduce_kernel<SoftmaxMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
     "row_reduce_kernel<WelfordMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
+    "row_scan_kernel<SoftmaxMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
+    "row_scan_kernel<WelfordMonoid>": "exact_io_aware_22_amd/csrc/reduce.hip",
     "delta_kernel + dq_kernel + dkdv_kernel": "exact_io_aware_22_amd/csrc/bwd_bf16.hip",
 }
 
@@ -392,7 +394,8 @@ def bench_reductions(steps: int, warmup: int, torch, fa, check: bool):
         rs = {"workload": name, "op": "inclusive scan", "ms": ms, "value": gbs, "unit": "GB/s",
               "roofline": {"kernel": skernel, "bound": "hbm", "achieved": gbs,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                           "traffic": None, "algorithmic_bytes_per_launch": nbytes}}
+                           "traffic": measured_traffic(skernel, name),
+                           "algorithmic_bytes_per_launch": nbytes}}
         if check:
             import oracle
 
