@@ -32,6 +32,8 @@
 // tile into every layout it is read in, so no registers hold staged data (dq_kernel:
 // K and V, 8 wavefronts, 256 query rows; dkdv_kernel: Q and dO, 8 wavefronts at D = 64,
 // 4 at D = 128). Two LDS slots, one barrier per tile.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -378,23 +380,26 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   };
   const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
 
-  auto step = [&](int g, const uint8_t* s) __attribute__((always_inline)) {
+  // Block g (32 queries) of the tile in slot s, in three phases: S and dP (MFMA), P and
+  // dS element-wise (VALU), then dV^T and dK^T (MFMA).
+  auto sdp = [&](int g, const uint8_t* s, f32x16_t& st, f32x16_t& dp) __attribute__((always_inline)) {
     const int b = (g & 1) * 32;
     const uint8_t* qr = s + b * G::RS + roff;
-    const uint8_t* qt = s + G::RT + b * G::CS + toff;
     const uint8_t* dr = s + G::RT + G::CT + b * G::RS + roff;
-    const uint8_t* dt = s + 2 * G::RT + G::CT + b * G::CS + toff;
-    const float* fl = reinterpret_cast<const float*>(s + 2 * G::RT + 2 * G::CT) + b;
-    f32x16_t st = f32x16_t{}, dp = f32x16_t{};
+    st = f32x16_t{};
+    dp = f32x16_t{};
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) {
       st = mfma(frag_row(qr, c2), as_bf16x8(kf[c2]), st);
       dp = mfma(frag_row(dr, c2), as_bf16x8(vf[c2]), dp);
     }
-    // Registers 8 cc + 4 h4 + k hold query 32 g + 16 cc + 8 half + 4 h4 + k: each group
-    // of four reads its four lse and Delta values just before use.
-    const bool masked = (32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32);
-    uint32_t pk[8], dsk[8];
+  };
+  // Registers 8 cc + 4 h4 + k hold query 32 g + 16 cc + 8 half + 4 h4 + k: each group
+  // of four reads its four lse and Delta values just before use.
+  // `masked` is a std::integral_constant: unmasked blocks carry no mask arithmetic.
+  auto ew = [&](int g, const uint8_t* s, const f32x16_t& st, const f32x16_t& dp, auto masked,
+                uint32_t (&pk)[8], uint32_t (&dsk)[8]) __attribute__((always_inline)) {
+    const float* fl = reinterpret_cast<const float*>(s + 2 * G::RT + 2 * G::CT) + (g & 1) * 32;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
             const int k = k2 + e, r = 8 * cc + 4 * h4 + k;
             const int q = 32 * g + 16 * cc + 8 * half + 4 * h4 + k;
             float sv = st[r];
-            if (masked && (q >= N || (CAUSAL && krow > q))) sv = kNegInf;
+            if (decltype(masked)::value && (q >= N || (CAUSAL && krow > q))) sv = kNegInf;
             pv[e] = exp2_hw(fmaf(sv, c, -l4[k]));
             dv2[e] = pv[e] * (dp[r] - d4[k]);
           }
@@ -419,6 +424,11 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
           dsk[i] = pack_bf16x2(dv2[0], dv2[1]);
         }
       }
+  };
+  auto acc = [&](int g, const uint8_t* s, const uint32_t (&pk)[8], const uint32_t (&dsk)[8]) __attribute__((always_inline)) {
+    const int b = (g & 1) * 32;
+    const uint8_t* qt = s + G::RT + b * G::CS + toff;
+    const uint8_t* dt = s + 2 * G::RT + G::CT + b * G::CS + toff;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const u32x4_t bp = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
@@ -429,6 +439,19 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
         dka[db] = mfma(frag_tr(qt, cc, db, G::CS), as_bf16x8(bs), dka[db]);
       }
     }
+  };
+  // One block: the diagonal and ragged blocks (queries past N, or below a key of this
+  // wavefront under the causal mask) take the masked variant, every other block one
+  // with no mask arithmetic.
+  auto step = [&](int g, const uint8_t* s) __attribute__((always_inline)) {
+    f32x16_t st, dp;
+    uint32_t pk[8], dsk[8];
+    sdp(g, s, st, dp);
+    if ((32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32))
+      ew(g, s, st, dp, std::true_type{}, pk, dsk);
+    else
+      ew(g, s, st, dp, std::false_type{}, pk, dsk);
+    acc(g, s, pk, dsk);
   };
 
   const int ntiles = k0 >= N ? 0 : ntiles_all - t_first;
