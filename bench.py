@@ -99,15 +99,77 @@ def time_launches(fn, steps: int, warmup: int, torch):
     return t0.elapsed_time(t1) / steps
 
 
-def bench_prefill(name: str, steps: int, warmup: int, torch, fa, make_inputs, W, check_rows=0):
+def time_each(fn, calls: int, torch):
+    """Per-call milliseconds, HIP events around each call on the current stream: the
+    median and the minimum over `calls` launches (run after time_launches, so warm)."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    mid = len(t) // 2
+    median = t[mid] if len(t) % 2 else 0.5 * (t[mid - 1] + t[mid])
+    return {"calls": calls, "median_ms": median, "min_ms": t[0]}
+
+
+def measured_ceilings(steps: int, warmup: int, torch, fa):
+    """The chip's sustained rates, the denominators of the fractions of measured (not
+    published) peaks: the library's MFMA-only loop (random bf16 register operands, two
+    wavefronts per SIMD) and its read-only stream (16-byte non-temporal loads of 2 GiB).
+    A bf16 GEMM (torch.mm) and a device copy are reported beside them as library
+    references."""
+    blocks, iters = 1024, 256
+    chk = torch.empty(blocks * 512, device="cuda")
+    ms_mfma = time_launches(lambda: fa.fa_calibrate_mfma(chk, blocks, iters, seed=1), steps,
+                            warmup, torch)
+    mfma_flops = 2 ** 19 * 8 * blocks * iters
+    nbytes = 2 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    rblocks = 1024
+    fold = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+    ms_read = time_launches(lambda: fa.fa_calibrate_read(x, fold, rblocks), steps, warmup, torch)
+    del chk, fold
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    ms_mm = time_launches(lambda: torch.mm(a, b, out=c), steps, warmup, torch)
+    del a, b, c
+    y = torch.empty_like(x)
+    ms_cp = time_launches(lambda: y.copy_(x), steps, warmup, torch)
+    del x, y
+    torch.cuda.empty_cache()
+    return {
+        "mfma_bf16_tflops": mfma_flops / (ms_mfma * 1e-3) / 1e12,
+        "mfma_bf16": f"fa_calibrate_mfma: {blocks} workgroups x 8 wavefronts x {iters} rounds "
+                     "of 16 32x32x16 bf16 products, random operands",
+        "read_gbs": nbytes / (ms_read * 1e-3) / 1e9,
+        "read": f"fa_calibrate_read: {nbytes >> 30} GiB, 16-byte non-temporal loads",
+        "library_reference": {
+            "bf16_gemm_tflops": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
+            "bf16_gemm": f"torch.mm {n}x{n}x{n}, N(0, 1) operands",
+            "copy_gbs": 2 * nbytes / (ms_cp * 1e-3) / 1e9,
+            "copy": f"device copy of {nbytes >> 30} GiB, bytes read + written"},
+    }
+
+
+def bench_prefill(name: str, steps: int, warmup: int, torch, fa, make_inputs, W, check_rows=0,
+                  per_launch=False):
     w = W[name]
     q, k, v = make_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o = torch.empty(w.B, w.H, w.N, w.D, dtype=torch.float32, device="cuda")
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
-    ms = time_launches(lambda: fa.fa_forward(qd, kd, vd, o, lse, w.scale, w.causal), steps, warmup,
-                       torch)
+    launch = lambda: fa.fa_forward(qd, kd, vd, o, lse, w.scale, w.causal)  # noqa: E731
+    ms = time_launches(launch, steps, warmup, torch)
     res = {"workload": name, "ms": ms, "tflops": w.flops() / (ms * 1e-3) / 1e12}
+    if per_launch:
+        res["per_launch"] = time_each(launch, max(20, steps), torch)
     if check_rows:
         res["parity"] = sampled_parity(w, q, k, v, o, lse, check_rows)
     del qd, kd, vd, o, lse
@@ -440,7 +502,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "masks",
-                                       "reductions", "copy"],
+                                       "reductions", "copy", "ceilings"],
                     default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -467,13 +529,17 @@ def main() -> int:
     if args.only == "copy":
         copy_calibration(torch, 1 << 30, args.steps)
         return 0
+    if args.only == "ceilings":
+        print(json.dumps({"ceilings": measured_ceilings(args.steps, args.warmup, torch, fa)}))
+        return 0
 
     out = {"metric": METRIC}
     if args.only in ("all", "prefill"):
         w = WORKLOADS[HEADLINE]
         log(f"timing {HEADLINE}")
         head, (q, k, v) = bench_prefill(HEADLINE, args.steps, args.warmup, torch, fa, make_inputs,
-                                        WORKLOADS, check_rows=64 if args.only == "all" else 0)
+                                        WORKLOADS, check_rows=64 if args.only == "all" else 0,
+                                        per_launch=True)
         ms = head["ms"]
         flops = w.flops()
         achieved = flops / (ms * 1e-3) / 1e12
@@ -491,6 +557,7 @@ def main() -> int:
         })
         if "parity" in head:
             out["parity"] = head["parity"]
+        out["per_launch"] = head["per_launch"]
         if args.only == "all" and not args.no_cpu_baseline:
             log("timing the fp64 oracle on host cores")
             out["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_seconds)
@@ -525,6 +592,20 @@ def main() -> int:
                         "dtype": "bf16", "data": "synthetic",
                         "config": {"workload": DECODE, "parallelism": "single GPU"},
                         "roofline": dec["roofline"]})
+    if args.only == "all":
+        # Measured last, so the headline is not timed on a clock the GEMM has heated.
+        log("timing the measured ceilings (MFMA-only loop, read stream, library references)")
+        ceil = measured_ceilings(10, 5, torch, fa)
+        out["ceilings"] = ceil
+        mfma_rooflines = [out.get("roofline"), out.get("backward", {}).get("roofline")]
+        for r in mfma_rooflines:
+            if r:
+                r["frac_of_measured"] = r["achieved"] / ceil["mfma_bf16_tflops"]
+        hbm_rooflines = [out.get("decode", {}).get("roofline")]
+        hbm_rooflines += [r.get("roofline") for r in out.get("reductions", [])]
+        for r in hbm_rooflines:
+            if r:
+                r["frac_of_measured"] = r["achieved"] / ceil["read_gbs"]
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)
     return 0

@@ -194,3 +194,24 @@ int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int 
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int fa_calibrate_mfma(float* out, int blocks, int iters, unsigned seed, void* stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 0) return FA_ERR_SHAPE;
+  if (!out) return FA_ERR_NULL;
+  if (!aligned(out, 4)) return FA_ERR_ALIGN;
+  return hip_status(
+      fa::launch_calibrate_mfma(out, blocks, iters, seed, static_cast<hipStream_t>(stream)));
+}
+
+int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks,
+                      void* stream) {
+  if (blocks < 1 || blocks > (1 << 22) || nbytes < 0 || nbytes % 16 != 0) return FA_ERR_SHAPE;
+  if (!out || (nbytes > 0 && !x)) return FA_ERR_NULL;
+  if (!aligned(out, 4) || !aligned(x, 16)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_calibrate_read(x, nbytes, out, blocks,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

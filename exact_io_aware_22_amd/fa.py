@@ -25,7 +25,7 @@ FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
             "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-            "fa_strerror", "fa_abi_version")
+            "fa_calibrate_mfma", "fa_calibrate_read", "fa_strerror", "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -60,6 +60,10 @@ def load():
     lib.fa_combine_partials.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_backward.restype = i
+    lib.fa_calibrate_mfma.argtypes = [vp, i, i, ctypes.c_uint, vp]
+    lib.fa_calibrate_mfma.restype = i
+    lib.fa_calibrate_read.argtypes = [vp, ctypes.c_longlong, vp, i, vp]
+    lib.fa_calibrate_read.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -212,6 +216,28 @@ def fa_moments_scan(x, mean, m2, stream=None) -> None:
     code = load().fa_moments_scan(_ptr(x), _ptr(mean), _ptr(m2), rows, n, _dtype_code(x),
                                   _stream(stream))
     _check(code, "fa_moments_scan")
+
+
+def fa_calibrate_mfma(out, blocks: int, iters: int, seed: int = 0, stream=None) -> None:
+    """Measurement only: the MFMA-only loop; out: fp32 [blocks * 512] (checksums).
+    One launch is 2**19 * 8 * blocks * iters flops."""
+    _dense(out)
+    if out.dtype != torch.float32 or out.numel() != blocks * 512:
+        raise ValueError("out must be float32 with blocks * 512 elements")
+    code = load().fa_calibrate_mfma(_ptr(out), int(blocks), int(iters), int(seed) & 0xFFFFFFFF,
+                                    _stream(stream))
+    _check(code, "fa_calibrate_mfma")
+
+
+def fa_calibrate_read(x, out, blocks: int, stream=None) -> None:
+    """Measurement only: a read-only stream over the bytes of x (a multiple of 16);
+    out: int32 [blocks * 256], each thread's XOR of the 32-bit words it read."""
+    _dense(x, out)
+    if out.dtype != torch.int32 or out.numel() != blocks * 256:
+        raise ValueError("out must be int32 with blocks * 256 elements")
+    nbytes = x.numel() * x.element_size()
+    code = load().fa_calibrate_read(_ptr(x), nbytes, _ptr(out), int(blocks), _stream(stream))
+    _check(code, "fa_calibrate_read")
 
 
 # ------------------------------------------------------------------ conveniences

@@ -215,6 +215,31 @@ int fa_softmax_scan(const void* x, float* m, float* d, int rows, int n, int dtyp
 int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int dtype,
                     void* stream);
 
+/*
+ * Measurement calls. They compute nothing of the method: they measure the chip's
+ * sustained rates on the two resources the kernels above are bound by, the measured
+ * roofline denominators reported beside the published peaks.
+ *
+ * fa_calibrate_mfma -- `blocks` workgroups of 8 wavefronts; each wavefront runs `iters`
+ * rounds of 16 bf16 matrix products 32x32x16 (8 independent float32 accumulators) on
+ * register operands of random bf16 values in +-[0.5, 4) drawn from `seed`. One launch
+ * is 2^19 * 8 * blocks * iters flops.
+ *   out : [blocks * 512] float32, written (each thread's accumulator sum, which keeps
+ *         the products from being elided; deterministic for a given seed).
+ *   1 <= blocks <= 2^20 and iters >= 0 (FA_ERR_SHAPE otherwise); out 4-byte aligned.
+ *
+ * fa_calibrate_read -- a read-only stream over x[0 .. nbytes) in 16-byte non-temporal
+ * loads by `blocks` workgroups of 256 threads. With n16 = nbytes / 16 words of 16 bytes
+ * and S = ceil(n16 / blocks) rounded up to a multiple of 256, workgroup b reads words
+ * [b S, min(n16, (b + 1) S)), its thread t those at offsets t, t + 256, t + 512, ...
+ *   out : [blocks * 256] uint32, written: out[256 b + t] is the XOR of the four 32-bit
+ *         words of every 16-byte word that thread read (0 if none).
+ *   nbytes >= 0 and a multiple of 16, 1 <= blocks <= 2^22 (FA_ERR_SHAPE otherwise);
+ *   x 16-byte aligned (may be NULL only when nbytes = 0), out 4-byte aligned.
+ */
+int fa_calibrate_mfma(float* out, int blocks, int iters, unsigned seed, void* stream);
+int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks, void* stream);
+
 /* Static, human-readable name of an FA_* code (never NULL). */
 const char* fa_strerror(int code);
 

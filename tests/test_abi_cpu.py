@@ -37,7 +37,7 @@ def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
          "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-         "fa_strerror", "fa_abi_version"])
+         "fa_calibrate_mfma", "fa_calibrate_read", "fa_strerror", "fa_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -206,3 +206,20 @@ def test_row_scan_validation(lib, which):
     assert red(lib, which, rows=0, x=None, o0=None, o1=None) == OK  # empty
     assert red(lib, which, n=0, x=None, o0=None, o1=None) == OK     # empty rows
     assert red(lib, which, rows=1 << 30, n=1 << 30) == SHAPE         # offsets overflow
+
+
+def test_calibration_validation(lib):
+    mf, rd = lib.fa_calibrate_mfma, lib.fa_calibrate_read
+    assert mf(None, 4, 1, 0, None) == NULL
+    assert mf(P, 0, 1, 0, None) == SHAPE
+    assert mf(P, (1 << 20) + 1, 1, 0, None) == SHAPE
+    assert mf(P, 4, -1, 0, None) == SHAPE
+    assert mf(P + 2, 4, 1, 0, None) == ALIGN
+    assert rd(P, 1024, None, 4, None) == NULL
+    assert rd(None, 1024, P, 4, None) == NULL
+    assert rd(P, 1000, P, 4, None) == SHAPE   # not a multiple of 16
+    assert rd(P, -16, P, 4, None) == SHAPE
+    assert rd(P, 1024, P, 0, None) == SHAPE
+    assert rd(P + 8, 1024, P, 4, None) == ALIGN
+    assert rd(P, 1024, P + 1, 4, None) == ALIGN
+

@@ -1,0 +1,61 @@
+"""The measurement calls (fa_calibrate_read, fa_calibrate_mfma) through the C ABI on one
+MI355X: the read stream's per-thread XOR is checked against the same fold computed on
+the host; the MFMA loop is checked for finite, seed-determined checksums."""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_22_amd import fa
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "these tests need the GPU"
+    fa.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def host_fold(words: np.ndarray, blocks: int) -> np.ndarray:
+    """XOR of the four 32-bit words of every 16-byte word, folded per reading thread:
+    workgroup b reads the words of its span [b S, (b + 1) S), S = ceil(n16 / blocks)
+    rounded up to a multiple of 256, thread t those at offsets t mod 256."""
+    v = np.bitwise_xor.reduce(words.reshape(-1, 4), axis=1)
+    span = -(-(-(-len(v) // blocks)) // 256) * 256
+    v = np.concatenate([v, np.zeros(blocks * span - len(v), dtype=v.dtype)])
+    return np.bitwise_xor.reduce(v.reshape(blocks, span // 256, 256), axis=1).reshape(-1)
+
+
+@pytest.mark.parametrize("n16,blocks", [(0, 3), (1, 2), (1000, 2), (1000, 7),
+                                        (4096 * 7 + 5, 8), (300, 64), (1 << 20, 64)])
+def test_read_stream_fold(n16, blocks):
+    print(f"calibrate_read n16={n16} blocks={blocks}", flush=True)
+    g = torch.Generator().manual_seed(n16 + blocks)
+    x = torch.randint(-2**31, 2**31 - 1, (max(1, 4 * n16),), generator=g, dtype=torch.int32)
+    x = x[:4 * n16]
+    xd = x.cuda()
+    out = torch.full((blocks * 256,), 7, dtype=torch.int32, device="cuda")
+    fa.fa_calibrate_read(xd, out, blocks)
+    torch.cuda.synchronize()
+    want = host_fold(x.numpy().view(np.uint32), blocks)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
+
+
+def test_mfma_loop_checksums():
+    print("calibrate_mfma blocks=16 iters=8", flush=True)
+    a = torch.empty(16 * 512, device="cuda")
+    b = torch.empty_like(a)
+    c = torch.empty_like(a)
+    fa.fa_calibrate_mfma(a, 16, 8, seed=1)
+    fa.fa_calibrate_mfma(b, 16, 8, seed=1)
+    fa.fa_calibrate_mfma(c, 16, 8, seed=2)
+    zero = torch.full_like(a, 5.0)
+    fa.fa_calibrate_mfma(zero, 16, 0, seed=1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all()
+    assert torch.equal(a, b)            # deterministic for a seed
+    assert not torch.equal(a, c)        # and the seed reaches the operands
+    assert (a != 0).float().mean() > 0.99
+    assert torch.equal(zero, torch.zeros_like(zero))  # no rounds: zero accumulators
