@@ -129,7 +129,7 @@ def measured_ceilings(steps: int, warmup: int, torch, fa):
     mfma_flops = 2 ** 19 * 8 * blocks * iters
     nbytes = 2 << 30
     x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-    rblocks = 1024
+    rblocks = 512
     fold = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
     ms_read = time_launches(lambda: fa.fa_calibrate_read(x, fold, rblocks), steps, warmup, torch)
     del chk, fold
