@@ -403,6 +403,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     alpha_prev = softmax(s_in, p_out);
   };
 
+  // The steady loop's step: the K fragments of the block its QK computes arrive in kf
+  // from the previous step, and the step loads those of the next step's block (knext)
+  // once its own products have taken them, so the LDS latency of a step's K reads
+  // overlaps the rest of the previous step (and, across a tile, its barrier).
+  auto step_pf = [&](int g, int knext, int vblk, f32x16_t& s_in, f32x16_t& s_out,
+                     const uint32_t (&p_in)[8], uint32_t (&p_out)[8]) __attribute__((always_inline)) {
+    (void)g;
+    rescale(alpha_prev);
+    s_out = qk(kf);
+    kload(knext, kf);
+    vload(vblk, vf);
+    pv(vf, p_in);
+    alpha_prev = softmax(s_in, p_out);
+  };
+
   // One iteration per tile t (blocks 2t and 2t+1). Slot offsets of K tiles t, t+1,
   // t+2 and of V tiles t-1, t, t+1 rotate through the three slots of each ring.
   // Tile t opens by issuing the direct loads of K tile t+2 and V tile t+1 and closes
@@ -456,12 +471,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll 1
   for (int t = t_lo; t < ntiles; ++t) {
     if (t == t_s0) {
+      // Block 2t + 1 (second half of K tile t) is the first the steady loop's QK takes;
+      // each step then loads the next: block 2t + 2 (first half of tile t + 1, resident
+      // during tile t) and block 2t + 3 (its second half, which is the slot ks0 + KH
+      // after the rotation). The last prefetch of the run is overwritten by the general
+      // tile that follows.
+      if (t < t_s1) kload(ks0 + KH, kf);
 #pragma unroll 1
       for (; t < t_s1; ++t) {
         dma(Kh, kring + ks2, CK, dk, t + 2, true);
         dma(Vh, vring + vs1, CV, dv, t + 1, true);
-        step(2 * t, ks0 + KH, vsp + VH, sa, sb, pa, pb, true);
-        step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, true);
+        step_pf(2 * t, ks1, vsp + VH, sa, sb, pa, pb);
+        step_pf(2 * t + 1, ks1 + KH, vs0, sb, sa, pb, pa);
         dma_wait();
         __syncthreads();
         rotate();
