@@ -319,15 +319,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // accumulator must be multiplied by before block g is added (1 if unchanged).
   // Weights of one block against the reference, packed to bf16 for the PV MFMA, with
   // their float32 sum (ps) and the sum of the packed values (pq).
-  auto weights = [&](const f32x16_t& s, float nmc, uint32_t (&pk)[8], float& ps, float& pq) __attribute__((always_inline)) {
+  // ps: the block's float32 sum (from its first pair, no add of a zero); pq: pq0 plus the
+  // sum of the packed values, so the running normaliser is carried through the chain.
+  auto weights = [&](const f32x16_t& s, float nmc, uint32_t (&pk)[8], float& ps, float& pq,
+                     float pq0) __attribute__((always_inline)) {
     const bf16x2_t ones = as_bf16x2(0x3f803f80u);
-    ps = 0.f;
-    pq = 0.f;
+    pq = pq0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p0 = exp2_hw(fmaf(s[2 * i], c, nmc));
       const float p1 = exp2_hw(fmaf(s[2 * i + 1], c, nmc));
-      ps += p0 + p1;
+      ps = i == 0 ? p0 + p1 : ps + (p0 + p1);
       pk[i] = pack_bf16x2(p0, p1);
       pq = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk[i]), ones, pq, false);
     }
@@ -337,10 +339,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // block, whose reference is -inf) does the wavefront take the rare path: the
   // block's maximum becomes the reference, O owes the factor alpha, and the block is
   // weighted again. No weight above 2^kTau is ever kept.
-  auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8]) __attribute__((always_inline)) {
+  // `resc` (wavefront-uniform) is set only on the rare path, so ordinary steps test a
+  // scalar flag instead of comparing a per-lane factor with 1.
+  auto softmax = [&](const f32x16_t& s, uint32_t (&pk)[8], bool& resc) __attribute__((always_inline)) {
     float ps, pq, alpha = 1.f;
-    weights(s, nmc_ref, pk, ps, pq);
+    resc = false;
+    weights(s, nmc_ref, pk, ps, pq, d_out);
     if (__builtin_amdgcn_ballot_w64(!(ps <= kSumLimit))) {
+      resc = true;
       float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
       for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
@@ -351,14 +357,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       // A row with no visible key yet keeps +inf, so its first finite score comes
       // back here; its masked scores get weight exp2(-inf) = 0 below.
       nmc_ref = m_new == kNegInf ? kInf : -m_new * c;
-      weights(s, m_new == kNegInf ? 0.f : nmc_ref, pk, ps, pq);
+      weights(s, m_new == kNegInf ? 0.f : nmc_ref, pk, ps, pq, d_out * alpha);
     }
     d_lse = fmaf(d_lse, alpha, ps);
-    d_out = fmaf(d_out, alpha, pq);
+    d_out = pq;
     return alpha;
   };
-  auto rescale = [&](float alpha) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+  auto rescale = [&](float alpha, bool resc) __attribute__((always_inline)) {
+    if (resc) {
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db) oacc[db] *= alpha;
     }
@@ -383,6 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   f32x16_t sa = f32x16_t{}, sb = f32x16_t{};
   uint32_t pa[8] = {0, 0, 0, 0, 0, 0, 0, 0}, pb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float alpha_prev = 1.f;  // factor O owes the reference of the latest softmax
+  bool resc_prev = false;  // whether it differs from 1 in some lane (uniform)
   u32x4_t kf[G::NCH], vf[2 * G::NDB];
 
   // Step g: scores of block g in s_in, weights of block g-1 in p_in; K block g+1 at
@@ -395,12 +402,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
                   const uint32_t (&p_in)[8], uint32_t (&p_out)[8], bool unmasked) __attribute__((always_inline)) {
     if (!unmasked && (g >= first_masked || g <= mask_lo_end)) apply_mask(g, s_in);
     // Bring O to the reference block g-1 was weighted against, then add PV(g-1).
-    rescale(alpha_prev);
+    rescale(alpha_prev, resc_prev);
     kload(kblk, kf);
     s_out = qk(kf);
     vload(vblk, vf);
     pv(vf, p_in);
-    alpha_prev = softmax(s_in, p_out);
+    alpha_prev = softmax(s_in, p_out, resc_prev);
   };
 
   // The steady loop's step: the K fragments of the block its QK computes arrive in kf
@@ -410,12 +417,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   auto step_pf = [&](int g, int knext, int vblk, f32x16_t& s_in, f32x16_t& s_out,
                      const uint32_t (&p_in)[8], uint32_t (&p_out)[8]) __attribute__((always_inline)) {
     (void)g;
-    rescale(alpha_prev);
+    rescale(alpha_prev, resc_prev);
     s_out = qk(kf);
     kload(knext, kf);
     vload(vblk, vf);
     pv(vf, p_in);
-    alpha_prev = softmax(s_in, p_out);
+    alpha_prev = softmax(s_in, p_out, resc_prev);
   };
 
   // One iteration per tile t (blocks 2t and 2t+1). Slot offsets of K tiles t, t+1,
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if (2 * t >= g_lo && 2 * t + 1 < nblk) step(2 * t + 1, ks1, vs0, sb, sa, pb, pa, false);
     if (nblk - 1 >= g_lo && (nblk - 1 == 2 * t || nblk - 1 == 2 * t + 1)) {
       // This wavefront's last block is in tile t: fold it in while its V is resident.
-      rescale(alpha_prev);
+      rescale(alpha_prev, resc_prev);
       vload(vs0 + ((nblk & 1) ? 0 : VH), vf);
       pv(vf, (nblk & 1) ? pb : pa);
     }
