@@ -504,6 +504,9 @@ def main() -> int:
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "masks",
                                        "reductions", "copy", "ceilings"],
                     default="all")
+    ap.add_argument("--workload", default=HEADLINE, choices=[HEADLINE] + EXTRA,
+                    help="with --only prefill: the prefill workload to time (default: the "
+                         "headline); its line then carries that workload's rate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -534,10 +537,14 @@ def main() -> int:
         return 0
 
     out = {"metric": METRIC}
+    if args.only != "prefill" and args.workload != HEADLINE:
+        print("--workload applies to --only prefill", file=sys.stderr)
+        return 2
     if args.only in ("all", "prefill"):
-        w = WORKLOADS[HEADLINE]
-        log(f"timing {HEADLINE}")
-        head, (q, k, v) = bench_prefill(HEADLINE, args.steps, args.warmup, torch, fa, make_inputs,
+        name = args.workload
+        w = WORKLOADS[name]
+        log(f"timing {name}")
+        head, (q, k, v) = bench_prefill(name, args.steps, args.warmup, torch, fa, make_inputs,
                                         WORKLOADS, check_rows=64 if args.only == "all" else 0,
                                         per_launch=True)
         ms = head["ms"]
@@ -547,12 +554,12 @@ def main() -> int:
             "value": achieved, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": HEADLINE, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+            "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                        "causal": w.causal, "sigma_qk": w.sigma_qk, "parallelism": "single GPU"},
             "roofline": {"kernel": "fwd_bf16_kernel", "bound": "mfma", "achieved": achieved,
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": achieved / PEAK_BF16_TFLOPS,
-                         "traffic": measured_traffic("fwd_bf16_kernel", HEADLINE),
+                         "traffic": measured_traffic("fwd_bf16_kernel", name),
                          "algorithmic_flops_per_launch": flops},
         })
         if "parity" in head:
