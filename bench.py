@@ -129,10 +129,17 @@ def measured_ceilings(steps: int, warmup: int, torch, fa):
     mfma_flops = 2 ** 19 * 8 * blocks * iters
     nbytes = 2 << 30
     x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-    rblocks = 512
-    fold = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
-    ms_read = time_launches(lambda: fa.fa_calibrate_read(x, fold, rblocks), steps, warmup, torch)
-    del chk, fold
+    # the streams' best grid: the best of a small sweep (one contiguous span per workgroup)
+    ms_read, ms_write = [], []
+    for rblocks in (512, 1024):
+        fold = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+        ms_read.append(time_launches(lambda: fa.fa_calibrate_read(x, fold, rblocks), steps,
+                                     warmup, torch))
+        ms_write.append(time_launches(lambda: fa.fa_calibrate_write(x, 7, rblocks), steps,
+                                      warmup, torch))
+        del fold
+    ms_read, ms_write = min(ms_read), min(ms_write)
+    del chk
     n = 8192
     g = torch.Generator(device="cuda").manual_seed(0)
     a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
@@ -149,7 +156,11 @@ def measured_ceilings(steps: int, warmup: int, torch, fa):
         "mfma_bf16": f"fa_calibrate_mfma: {blocks} workgroups x 8 wavefronts x {iters} rounds "
                      "of 16 32x32x16 bf16 products, random operands",
         "read_gbs": nbytes / (ms_read * 1e-3) / 1e9,
-        "read": f"fa_calibrate_read: {nbytes >> 30} GiB, 16-byte non-temporal loads",
+        "read": f"fa_calibrate_read: {nbytes >> 30} GiB, 16-byte non-temporal loads, best of "
+                "512 and 1024 workgroups",
+        "write_gbs": nbytes / (ms_write * 1e-3) / 1e9,
+        "write": f"fa_calibrate_write: {nbytes >> 30} GiB, 16-byte non-temporal stores, best of "
+                 "512 and 1024 workgroups",
         "library_reference": {
             "bf16_gemm_tflops": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
             "bf16_gemm": f"torch.mm {n}x{n}x{n}, N(0, 1) operands",
@@ -246,7 +257,8 @@ def bench_decode(steps: int, warmup: int, torch, fa, make_inputs, W):
         "config": {"B": w.B, "H": w.H, "L": w.L, "D": w.D, "splits": S, "dtype": "bf16"},
         "roofline": {"kernel": "decode_partials_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes,
+                     "read_bytes": part_bytes, "write_bytes": BH * S * (D + 2) * 4},
         "parity": {"heads": len(heads), "max_abs_err_o": max(errs_o), "max_abs_err_lse": max(errs_l)},
     }
     del qd, kd, vd
@@ -426,7 +438,8 @@ def bench_reductions(steps: int, warmup: int, torch, fa, check: bool):
              "roofline": {"kernel": kernel, "bound": "hbm", "achieved": gbs,
                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                           "traffic": measured_traffic(kernel, name),
-                          "algorithmic_bytes_per_launch": nbytes}}
+                          "algorithmic_bytes_per_launch": nbytes,
+                          "read_bytes": w.bytes_read(), "write_bytes": w.bytes_written()}}
         if check:
             import oracle
 
@@ -457,7 +470,8 @@ def bench_reductions(steps: int, warmup: int, torch, fa, check: bool):
               "roofline": {"kernel": skernel, "bound": "hbm", "achieved": gbs,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                            "traffic": measured_traffic(skernel, name),
-                           "algorithmic_bytes_per_launch": nbytes}}
+                           "algorithmic_bytes_per_launch": nbytes,
+                           "read_bytes": w.bytes_read(), "write_bytes": 2 * 4 * w.rows * w.n}}
         if check:
             import oracle
 
@@ -601,7 +615,7 @@ def main() -> int:
                         "roofline": dec["roofline"]})
     if args.only == "all":
         # Measured last, so the headline is not timed on a clock the GEMM has heated.
-        log("timing the measured ceilings (MFMA-only loop, read stream, library references)")
+        log("timing the measured ceilings (MFMA-only loop, read and write streams, library references)")
         ceil = measured_ceilings(10, 5, torch, fa)
         out["ceilings"] = ceil
         mfma_rooflines = [out.get("roofline"), out.get("backward", {}).get("roofline")]
@@ -612,7 +626,11 @@ def main() -> int:
         hbm_rooflines += [r.get("roofline") for r in out.get("reductions", [])]
         for r in hbm_rooflines:
             if r:
-                r["frac_of_measured"] = r["achieved"] / ceil["read_gbs"]
+                # the time a read stream and a write stream of the same bytes would take,
+                # over the measured time
+                t_ceil = (r["read_bytes"] / ceil["read_gbs"] + r["write_bytes"] / ceil["write_gbs"])
+                t_meas = r["algorithmic_bytes_per_launch"] / r["achieved"]
+                r["frac_of_measured"] = t_ceil / t_meas
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)
     return 0

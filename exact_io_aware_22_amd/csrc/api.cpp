@@ -214,4 +214,13 @@ int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks
                                               static_cast<hipStream_t>(stream)));
 }
 
+int fa_calibrate_write(void* y, long long nbytes, unsigned value, int blocks, void* stream) {
+  if (blocks < 1 || blocks > (1 << 22) || nbytes < 0 || nbytes % 16 != 0) return FA_ERR_SHAPE;
+  if (nbytes == 0) return FA_OK;  // empty: no pointer is touched, nothing is launched
+  if (!y) return FA_ERR_NULL;
+  if (!aligned(y, 16)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_calibrate_write(y, nbytes, value, blocks,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

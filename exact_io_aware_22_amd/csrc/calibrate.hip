@@ -9,6 +9,8 @@
 //   * read_stream_kernel: 16-byte non-temporal loads of a buffer, each workgroup over
 //     one contiguous span, eight in flight per thread, XOR-folded so the loads cannot
 //     be elided.
+//   * write_stream_kernel: the same split with 16-byte non-temporal stores of a
+//     checkable pattern.
 #include "device.h"
 #include "launch.h"
 
@@ -90,6 +92,26 @@ __global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4_t
   out[int64_t(blockIdx.x) * kReadThreads + threadIdx.x] = acc;
 }
 
+// Workgroup b writes the 16-byte words of its span (the same split as the read stream),
+// thread t those at positions t mod 256, eight stores in flight; every word gets
+// {value, word index (low 32 bits), value, word index} so the result can be checked.
+__global__ __launch_bounds__(kReadThreads) void write_stream_kernel(u32x4_t* __restrict__ y,
+                                                                    int64_t n16, int64_t span,
+                                                                    uint32_t value) {
+  const int64_t b0 = int64_t(blockIdx.x) * span;
+  const int64_t end = min(n16, b0 + span);
+  int64_t i = b0 + threadIdx.x;
+  for (; i + 7 * kReadThreads < end; i += 8 * kReadThreads) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = uint32_t(i + j * kReadThreads);
+      __builtin_nontemporal_store(u32x4_t{value, w, value, w}, y + i + j * kReadThreads);
+    }
+  }
+  for (; i < end; i += kReadThreads)
+    __builtin_nontemporal_store(u32x4_t{value, uint32_t(i), value, uint32_t(i)}, y + i);
+}
+
 }  // namespace
 
 hipError_t launch_calibrate_mfma(float* out, int blocks, int iters, uint32_t seed,
@@ -106,6 +128,15 @@ hipError_t launch_calibrate_read(const void* x, int64_t nbytes, uint32_t* out, i
   const int64_t span = ((n16 + blocks - 1) / blocks + kReadThreads - 1) / kReadThreads * kReadThreads;
   hipLaunchKernelGGL(read_stream_kernel, dim3(unsigned(blocks)), dim3(kReadThreads), 0, s,
                      static_cast<const u32x4_t*>(x), n16, span, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate_write(void* y, int64_t nbytes, uint32_t value, int blocks,
+                                  hipStream_t s) {
+  const int64_t n16 = nbytes / 16;
+  const int64_t span = ((n16 + blocks - 1) / blocks + kReadThreads - 1) / kReadThreads * kReadThreads;
+  hipLaunchKernelGGL(write_stream_kernel, dim3(unsigned(blocks)), dim3(kReadThreads), 0, s,
+                     static_cast<u32x4_t*>(y), n16, span, value);
   return hipGetLastError();
 }
 

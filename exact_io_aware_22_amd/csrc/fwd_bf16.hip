@@ -258,8 +258,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // block, chunk 2c + half. V^T operand (transposing read): key 8*half + j/4 and
   // head dims 16*((lane>>4)&1) + 4*(j%4) for lane j = lane % 16 of its group.
   const int koff = swap23(l32) * G::KSTRIDE + half * 16;
-  const int voff = (8 * half + ((lane & 15) >> 2)) * G::VSTRIDE +
-                   (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // voffr: the same offset from the start of LDS, i.e. with the V ring's base included,
+  // kept opaque to the compiler so the base is added once here rather than folded into
+  // the reads' immediates (which it would overflow, costing a second add per step).
+  int voffr = kSlots * G::KTILE + (8 * half + ((lane & 15) >> 2)) * G::VSTRIDE +
+              (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  asm volatile("" : "+v"(voffr));
 
   // Fragments of S^T block g (32 keys x this wavefront's 32 queries): the K operand
   // rows from the K ring, one 16-byte read per 16-wide chunk of the head dim.
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // O^T += V^T (block g) P^T (block g). A operand rows: head dims 32db + l32; k:
   // keys 16cc + 8*half + 0..7 of the block, from two transposing reads.
   auto vload = [&](int voff_blk, u32x4_t (&vf)[2 * G::NDB]) __attribute__((always_inline)) {
-    const uint8_t* vb = vring + voff_blk + voff;
+    const uint8_t* vb = smem + voff_blk + voffr;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll

@@ -25,7 +25,8 @@ FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
             "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-            "fa_calibrate_mfma", "fa_calibrate_read", "fa_strerror", "fa_abi_version")
+            "fa_calibrate_mfma", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
+            "fa_abi_version")
 
 
 class FaError(RuntimeError):
@@ -64,6 +65,8 @@ def load():
     lib.fa_calibrate_mfma.restype = i
     lib.fa_calibrate_read.argtypes = [vp, ctypes.c_longlong, vp, i, vp]
     lib.fa_calibrate_read.restype = i
+    lib.fa_calibrate_write.argtypes = [vp, ctypes.c_longlong, ctypes.c_uint, i, vp]
+    lib.fa_calibrate_write.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -238,6 +241,16 @@ def fa_calibrate_read(x, out, blocks: int, stream=None) -> None:
     nbytes = x.numel() * x.element_size()
     code = load().fa_calibrate_read(_ptr(x), nbytes, _ptr(out), int(blocks), _stream(stream))
     _check(code, "fa_calibrate_read")
+
+
+def fa_calibrate_write(y, value: int, blocks: int, stream=None) -> None:
+    """Measurement only: a write-only stream over the bytes of y (a multiple of 16);
+    16-byte word w becomes {value, w, value, w} as 32-bit words."""
+    _dense(y)
+    nbytes = y.numel() * y.element_size()
+    code = load().fa_calibrate_write(_ptr(y), nbytes, int(value) & 0xFFFFFFFF, int(blocks),
+                                     _stream(stream))
+    _check(code, "fa_calibrate_write")
 
 
 # ------------------------------------------------------------------ conveniences

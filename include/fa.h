@@ -239,6 +239,15 @@ int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int 
  */
 int fa_calibrate_mfma(float* out, int blocks, int iters, unsigned seed, void* stream);
 int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks, void* stream);
+/*
+ * fa_calibrate_write -- a write-only stream over y[0 .. nbytes) in 16-byte non-temporal
+ * stores, split over `blocks` workgroups of 256 threads as fa_calibrate_read splits its
+ * reads. The 16-byte word w (w = 0, 1, ...) is written as the four 32-bit words
+ * {value, w mod 2^32, value, w mod 2^32}.
+ *   nbytes >= 0 and a multiple of 16, 1 <= blocks <= 2^22 (FA_ERR_SHAPE otherwise);
+ *   y 16-byte aligned. nbytes = 0 returns FA_OK at once (y may then be NULL).
+ */
+int fa_calibrate_write(void* y, long long nbytes, unsigned value, int blocks, void* stream);
 
 /* Static, human-readable name of an FA_* code (never NULL). */
 const char* fa_strerror(int code);

@@ -37,7 +37,8 @@ def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
          "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-         "fa_calibrate_mfma", "fa_calibrate_read", "fa_strerror", "fa_abi_version"])
+         "fa_calibrate_mfma", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
+         "fa_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -222,4 +223,10 @@ def test_calibration_validation(lib):
     assert rd(P, 1024, P, 0, None) == SHAPE
     assert rd(P + 8, 1024, P, 4, None) == ALIGN
     assert rd(P, 1024, P + 1, 4, None) == ALIGN
+    wr = lib.fa_calibrate_write
+    assert wr(None, 1024, 1, 4, None) == NULL
+    assert wr(None, 0, 1, 4, None) == OK     # empty: returns before any HIP call
+    assert wr(P, 1000, 1, 4, None) == SHAPE
+    assert wr(P, 1024, 1, 0, None) == SHAPE
+    assert wr(P + 8, 1024, 1, 4, None) == ALIGN
 

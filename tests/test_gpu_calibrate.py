@@ -59,3 +59,18 @@ def test_mfma_loop_checksums():
     assert not torch.equal(a, c)        # and the seed reaches the operands
     assert (a != 0).float().mean() > 0.99
     assert torch.equal(zero, torch.zeros_like(zero))  # no rounds: zero accumulators
+
+
+@pytest.mark.parametrize("n16,blocks", [(1, 2), (1000, 7), (4096 * 7 + 5, 8), (1 << 20, 64)])
+def test_write_stream_pattern(n16, blocks):
+    print(f"calibrate_write n16={n16} blocks={blocks}", flush=True)
+    y = torch.zeros(4 * n16 + 8, dtype=torch.int32, device="cuda")
+    body = y[:4 * n16]
+    fa.fa_calibrate_write(body, 0x5EED1234, blocks)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().view(np.uint32)
+    w = np.arange(n16, dtype=np.uint64).astype(np.uint32)
+    want = np.stack([np.full(n16, 0x5EED1234, np.uint32), w,
+                     np.full(n16, 0x5EED1234, np.uint32), w], axis=1).reshape(-1)
+    assert np.array_equal(got[:4 * n16], want)
+    assert not got[4 * n16:].any()  # nothing past the end
