@@ -6,7 +6,8 @@
 // out once as o / d with lse = M + ln D.
 //
 // decode_partials is a pure stream over K and V (about one flop per byte), so it is
-// laid out for HBM: one workgroup per (head, chunk), four wavefronts each taking
+// laid out for HBM: a workgroup folds kUnits consecutive (head, chunk) units, one
+// after the other, four wavefronts each taking
 // 16*R keys per step with non-temporal 16-byte loads that tile whole key rows (R rows
 // per wave-wide load), K and V requests issued together, dot products finished with
 // cross-lane adds inside a row, and the four wavefronts' states merged in LDS.
@@ -18,12 +19,17 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kLoads = 16;  // 16-byte loads per lane per step, per tensor
+// (head, chunk) units per workgroup: consecutive units are consecutive chunks of one
+// head, so a workgroup streams one longer contiguous span of K and V. Two measured
+// best at the decode workload (1 to 8 tried: 8 and 4 lose more to the last
+// workgroups' tail than they gain from longer spans).
+constexpr int kUnits = 2;
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(64 * kWaves) void decode_partials_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     float* __restrict__ Mo, float* __restrict__ Do, float* __restrict__ Op, int L, int splits,
-    int chunk, float c, float scale) {
+    int64_t units, int chunk, float c, float scale) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int E = 16 / ESZ;       // elements per 16-byte load
   constexpr int LPR = D / E;        // lanes per key row
@@ -33,127 +39,133 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partials_kernel(
   __shared__ __attribute__((aligned(16))) float sm_o[kWaves][D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x % splits;
-  const int64_t bh = blockIdx.x / splits;
-  const int64_t j0l = int64_t(split) * chunk;
-  const int j0 = int(j0l < L ? j0l : L);
-  const int j1 = int(j0l + chunk < L ? j0l + chunk : L);
-  const int row = lane / LPR, col = (lane % LPR) * E;
-  const int64_t rowbytes = int64_t(D) * ESZ;
-  const uint8_t* Kh = K + bh * L * rowbytes + col * ESZ;
-  const uint8_t* Vh = V + bh * L * rowbytes + col * ESZ;
-  const u32x4_t qw = load16(Q + bh * rowbytes + col * ESZ);
+  for (int t = 0; t < kUnits; ++t) {
+    const int64_t unit = int64_t(blockIdx.x) * kUnits + t;
+    if (unit >= units) break;  // uniform: every thread of the workgroup sees the same unit
+    const int split = int(unit % splits);
+    const int64_t bh = unit / splits;
+    const int64_t j0l = int64_t(split) * chunk;
+    const int j0 = int(j0l < L ? j0l : L);
+    const int j1 = int(j0l + chunk < L ? j0l + chunk : L);
+    const int row = lane / LPR, col = (lane % LPR) * E;
+    const int64_t rowbytes = int64_t(D) * ESZ;
+    const uint8_t* Kh = K + bh * L * rowbytes + col * ESZ;
+    const uint8_t* Vh = V + bh * L * rowbytes + col * ESZ;
+    const u32x4_t qw = load16(Q + bh * rowbytes + col * ESZ);
 
-  float m_run = kNegInf, d_run = 0.f;
-  float o[E];
+    float m_run = kNegInf, d_run = 0.f;
+    float o[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
 
-  for (int jb = j0 + wave * KW; jb < j1; jb += kWaves * KW) {
-    u32x4_t kr[kLoads], vr[kLoads];
+    for (int jb = j0 + wave * KW; jb < j1; jb += kWaves * KW) {
+      u32x4_t kr[kLoads], vr[kLoads];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int key = jb + i * RPW + row;
-      const bool ok = key < j1;
-      // Non-temporal: K and V are read once, so nothing is kept in the caches.
-      kr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kh + int64_t(key) * rowbytes))
-                 : u32x4_t{0, 0, 0, 0};
-      vr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vh + int64_t(key) * rowbytes))
-                 : u32x4_t{0, 0, 0, 0};
-    }
-    float s[kLoads];
-    float mx = kNegInf;
+      for (int i = 0; i < kLoads; ++i) {
+        const int key = jb + i * RPW + row;
+        const bool ok = key < j1;
+        // Non-temporal: K and V are read once, so nothing is kept in the caches.
+        kr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kh + int64_t(key) * rowbytes))
+                   : u32x4_t{0, 0, 0, 0};
+        vr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vh + int64_t(key) * rowbytes))
+                   : u32x4_t{0, 0, 0, 0};
+      }
+      float s[kLoads];
+      float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      float p = 0.f;
-      if constexpr (BF16) {
+      for (int i = 0; i < kLoads; ++i) {
+        float p = 0.f;
+        if constexpr (BF16) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          p = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[i][w]), as_bf16x2(qw[w]), p, false);
-      } else {
+          for (int w = 0; w < 4; ++w)
+            p = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[i][w]), as_bf16x2(qw[w]), p, false);
+        } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) p = fmaf(__uint_as_float(kr[i][w]), __uint_as_float(qw[w]), p);
+          for (int w = 0; w < 4; ++w) p = fmaf(__uint_as_float(kr[i][w]), __uint_as_float(qw[w]), p);
+        }
+#pragma unroll
+        for (int off = 1; off < LPR; off <<= 1) p += __shfl_xor(p, off);
+        s[i] = (jb + i * RPW + row < j1) ? p : kNegInf;
+        mx = fmaxf(mx, s[i]);
       }
 #pragma unroll
-      for (int off = 1; off < LPR; off <<= 1) p += __shfl_xor(p, off);
-      s[i] = (jb + i * RPW + row < j1) ? p : kNegInf;
-      mx = fmaxf(mx, s[i]);
-    }
+      for (int off = LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_new = fmaxf(m_run, mx);
+      const float mref = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_hw((m_run - mref) * c);
+      const float nmc = -mref * c;
+      d_run *= alpha;
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float m_new = fmaxf(m_run, mx);
-    const float mref = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2_hw((m_run - mref) * c);
-    const float nmc = -mref * c;
-    d_run *= alpha;
+      for (int e = 0; e < E; ++e) o[e] *= alpha;
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] *= alpha;
+      for (int i = 0; i < kLoads; ++i) {
+        const float p = exp2_hw(fmaf(s[i], c, nmc));
+        d_run += p;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const float p = exp2_hw(fmaf(s[i], c, nmc));
-      d_run += p;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if constexpr (BF16) {
-          o[2 * w] = fmaf(p, bf16_lo(vr[i][w]), o[2 * w]);
-          o[2 * w + 1] = fmaf(p, bf16_hi(vr[i][w]), o[2 * w + 1]);
-        } else {
-          o[w] = fmaf(p, __uint_as_float(vr[i][w]), o[w]);
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (BF16) {
+            o[2 * w] = fmaf(p, bf16_lo(vr[i][w]), o[2 * w]);
+            o[2 * w + 1] = fmaf(p, bf16_hi(vr[i][w]), o[2 * w + 1]);
+          } else {
+            o[w] = fmaf(p, __uint_as_float(vr[i][w]), o[w]);
+          }
         }
       }
+      m_run = m_new;
     }
-    m_run = m_new;
-  }
 
-  // Sum the rows of this wavefront (same m everywhere in the wavefront).
+    // Sum the rows of this wavefront (same m everywhere in the wavefront).
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-    d_run += __shfl_xor(d_run, off);
+    for (int off = LPR; off < 64; off <<= 1) {
+      d_run += __shfl_xor(d_run, off);
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] += __shfl_xor(o[e], off);
-  }
-  if (lane < LPR) {
+      for (int e = 0; e < E; ++e) o[e] += __shfl_xor(o[e], off);
+    }
+    if (lane < LPR) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) sm_o[wave][col + e] = o[e];
-  }
-  if (lane == 0) {
-    sm_m[wave] = m_run;
-    sm_d[wave] = d_run;
-  }
-  __syncthreads();
+      for (int e = 0; e < E; ++e) sm_o[wave][col + e] = o[e];
+    }
+    if (lane == 0) {
+      sm_m[wave] = m_run;
+      sm_d[wave] = d_run;
+    }
+    __syncthreads();
 
-  // Merge the wavefronts' states; write m in natural-log units of the scaled score.
-  if (tid < D) {
-    float M = kNegInf;
+    // Merge the wavefronts' states; write m in natural-log units of the scaled score.
+    if (tid < D) {
+      float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w]);
-    const float mref = M == kNegInf ? 0.f : M;
-    float den = 0.f, acc = 0.f;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w]);
+      const float mref = M == kNegInf ? 0.f : M;
+      float den = 0.f, acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2_hw((sm_m[w] - mref) * c);
-      den = fmaf(f, sm_d[w], den);
-      acc = fmaf(f, sm_o[w][tid], acc);
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2_hw((sm_m[w] - mref) * c);
+        den = fmaf(f, sm_d[w], den);
+        acc = fmaf(f, sm_o[w][tid], acc);
+      }
+      const int64_t out = bh * splits + split;
+      Op[out * D + tid] = acc;
+      if (tid == 0) {
+        Mo[out] = M == kNegInf ? kNegInf : M * scale;
+        Do[out] = den;
+      }
     }
-    const int64_t out = bh * splits + split;
-    Op[out * D + tid] = acc;
-    if (tid == 0) {
-      Mo[out] = M == kNegInf ? kNegInf : M * scale;
-      Do[out] = den;
-    }
+    __syncthreads();  // the next unit rewrites the merge buffers
   }
 }
 
 template <bool BF16, int D>
 hipError_t launch_partials(const DecodeArgs& a, hipStream_t s) {
   const int64_t BH = int64_t(a.B) * a.H;
-  const int64_t blocks = BH * a.splits;
+  const int64_t units = BH * a.splits;
+  const int64_t blocks = (units + kUnits - 1) / kUnits;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int chunk = int((int64_t(a.L) + a.splits - 1) / a.splits);
   hipLaunchKernelGGL((decode_partials_kernel<BF16, D>), dim3(unsigned(blocks)), dim3(64 * kWaves),
                      0, s, static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
-                     static_cast<const uint8_t*>(a.v), a.m, a.d, a.o_part, a.L, a.splits, chunk,
-                     a.scale * kLog2e, a.scale);
+                     static_cast<const uint8_t*>(a.v), a.m, a.d, a.o_part, a.L, a.splits, units,
+                     chunk, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
