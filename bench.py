@@ -99,6 +99,24 @@ def time_launches(fn, steps: int, warmup: int, torch):
     return t0.elapsed_time(t1) / steps
 
 
+def stream_fraction(read_bytes: float, write_bytes: float, alg_bytes: float, achieved_gbs: float,
+                    read_gbs: float, write_gbs: float) -> float:
+    """Fraction of the measured HBM ceiling for a kernel that reads read_bytes and writes
+    write_bytes per launch and whose roofline reports achieved_gbs over alg_bytes: the
+    time a read stream and a write stream of those bytes take (at read_gbs, write_gbs),
+    over the kernel's measured time (alg_bytes / achieved_gbs)."""
+    t_ceiling = read_bytes / read_gbs + write_bytes / write_gbs
+    t_measured = alg_bytes / achieved_gbs
+    return t_ceiling / t_measured
+
+
+def median_min(times_ms):
+    """Median (mean of the middle two for an even count) and minimum of per-call times."""
+    t = sorted(times_ms)
+    mid = len(t) // 2
+    return (t[mid] if len(t) % 2 else 0.5 * (t[mid - 1] + t[mid])), t[0]
+
+
 def time_each(fn, calls: int, torch):
     """Per-call milliseconds, HIP events around each call on the current stream: the
     median and the minimum over `calls` launches (run after time_launches, so warm)."""
@@ -110,10 +128,8 @@ def time_each(fn, calls: int, torch):
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) for a, b in ev)
-    mid = len(t) // 2
-    median = t[mid] if len(t) % 2 else 0.5 * (t[mid - 1] + t[mid])
-    return {"calls": calls, "median_ms": median, "min_ms": t[0]}
+    median, fastest = median_min([a.elapsed_time(b) for a, b in ev])
+    return {"calls": calls, "median_ms": median, "min_ms": fastest}
 
 
 def measured_ceilings(steps: int, warmup: int, torch, fa):
@@ -626,11 +642,9 @@ def main() -> int:
         hbm_rooflines += [r.get("roofline") for r in out.get("reductions", [])]
         for r in hbm_rooflines:
             if r:
-                # the time a read stream and a write stream of the same bytes would take,
-                # over the measured time
-                t_ceil = (r["read_bytes"] / ceil["read_gbs"] + r["write_bytes"] / ceil["write_gbs"])
-                t_meas = r["algorithmic_bytes_per_launch"] / r["achieved"]
-                r["frac_of_measured"] = t_ceil / t_meas
+                r["frac_of_measured"] = stream_fraction(
+                    r["read_bytes"], r["write_bytes"], r["algorithmic_bytes_per_launch"],
+                    r["achieved"], ceil["read_gbs"], ceil["write_gbs"])
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)
     return 0

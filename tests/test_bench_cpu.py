@@ -33,3 +33,28 @@ def test_published_peaks():
     assert bench.PEAK_BF16_TFLOPS == 2500.0  # dense bf16 MFMA
     assert bench.PEAK_HBM_GBS == 8000.0      # HBM3E
     assert bench.HEADLINE == "large_score_causal_d128"
+
+
+def test_stream_fraction_against_the_two_ceilings():
+    sys.path.insert(0, str(ROOT))
+    import bench
+
+    # Units cancel, so plain numbers: ceilings 7 (read) and 5 (write) bytes per time
+    # unit. A kernel reading 1 and writing 4 at exactly the ceilings takes 1/7 + 4/5;
+    # its roofline over all 5 bytes then reports 5 / (1/7 + 4/5).
+    t = 1 / 7 + 4 / 5
+    assert abs(bench.stream_fraction(1, 4, 5, 5 / t, 7, 5) - 1.0) < 1e-12
+    assert abs(bench.stream_fraction(1, 4, 5, 5 / (2 * t), 7, 5) - 0.5) < 1e-12  # twice as slow
+    # A roofline that credits only the reads (as the decode's does): the writes still
+    # take ceiling time.
+    t = 1 / 7 + 0.01 / 5
+    assert abs(bench.stream_fraction(1, 0.01, 1, 1 / t, 7, 5) - 1.0) < 1e-12
+
+
+def test_median_and_min():
+    sys.path.insert(0, str(ROOT))
+    import bench
+
+    assert bench.median_min([3.0, 1.0, 2.0]) == (2.0, 1.0)
+    assert bench.median_min([4.0, 1.0, 3.0, 2.0]) == (2.5, 1.0)
+
