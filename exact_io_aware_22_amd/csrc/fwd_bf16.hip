@@ -418,9 +418,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   // from the previous step, and the step loads those of the next step's block (knext)
   // once its own products have taken them, so the LDS latency of a step's K reads
   // overlaps the rest of the previous step (and, across a tile, its barrier).
-  auto step_pf = [&](int g, int knext, int vblk, f32x16_t& s_in, f32x16_t& s_out,
+  auto step_pf = [&](int knext, int vblk, f32x16_t& s_in, f32x16_t& s_out,
                      const uint32_t (&p_in)[8], uint32_t (&p_out)[8]) __attribute__((always_inline)) {
-    (void)g;
     rescale(alpha_prev, resc_prev);
     s_out = qk(kf);
     kload(knext, kf);
@@ -492,8 +491,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       for (; t < t_s1; ++t) {
         dma(Kh, kring + ks2, CK, dk, t + 2, true);
         dma(Vh, vring + vs1, CV, dv, t + 1, true);
-        step_pf(2 * t, ks1, vsp + VH, sa, sb, pa, pb);
-        step_pf(2 * t + 1, ks1 + KH, vs0, sb, sa, pb, pa);
+        step_pf(ks1, vsp + VH, sa, sb, pa, pb);       // blocks 2t (softmax), 2t+1 (QK)
+        step_pf(ks1 + KH, vs0, sb, sa, pb, pa);       // blocks 2t+1, 2t+2
         dma_wait();
         __syncthreads();
         rotate();
