@@ -225,6 +225,13 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
   f32x16_t acc[G::NDB];
 #pragma unroll
   for (int db = 0; db < G::NDB; ++db) acc[db] = f32x16_t{};
+  // At D = 128 the dP^T products accumulate onto -Delta (one value per lane: its query),
+  // so they yield dP - Delta directly and dS needs one multiply per element. (At D = 64
+  // the 16 registers would cost the second workgroup per CU.)
+  constexpr bool kFoldDelta = D == 128;
+  f32x16_t ndl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = kFoldDelta ? -dl : 0.f;
 
   // Staging: chunk i of a thread is row (tid + 256 i) / CPR, column (tid + 256 i) % CPR
   // of the 64-key tile; rows past the end read the last row (finite; masked below).
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
     const uint8_t* kr = s + b * G::RS + roff;
     const uint8_t* kt = s + G::RT + b * G::CS + toff;
     const uint8_t* vr = s + G::RT + G::CT + b * G::RS + roff;
-    f32x16_t st = f32x16_t{}, dp = f32x16_t{};
+    f32x16_t st = f32x16_t{}, dp = ndl;
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) {
       st = mfma(frag_row(kr, c2), as_bf16x8(qf[c2]), st);
@@ -263,7 +270,10 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
     for (int i = 0; i < 8; ++i) {
       const float p0 = exp2_hw(fmaf(st[2 * i], c, -lse2));
       const float p1 = exp2_hw(fmaf(st[2 * i + 1], c, -lse2));
-      ds[i] = pack_bf16x2(p0 * (dp[2 * i] - dl), p1 * (dp[2 * i + 1] - dl));
+      if constexpr (kFoldDelta)
+        ds[i] = pack_bf16x2(p0 * dp[2 * i], p1 * dp[2 * i + 1]);
+      else
+        ds[i] = pack_bf16x2(p0 * (dp[2 * i] - dl), p1 * (dp[2 * i + 1] - dl));
     }
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
