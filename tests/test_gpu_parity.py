@@ -303,6 +303,30 @@ def test_decode_sizes(dtype, D, L, splits):
     check(o, lse, o_ref.reshape(6, D), lse_ref.reshape(6), dtype, f"decode L={L} splits={splits}")
 
 
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("B,H,L,splits", [(1, 1, 200, 1), (1, 3, 300, 5), (1, 1, 513, 3),
+                                          (3, 1, 1000, 7)])
+def test_decode_odd_unit_counts(dtype, D, B, H, L, splits):
+    """B * H * splits odd: a workgroup folds two (head, chunk) units in turn, so the last
+    workgroup has a single unit and must stop after it."""
+    seed = 11 * L + splits + B
+    q = random_tensor((B, H, 1, D), seed, dtype)
+    k = random_tensor((B, H, L, D), seed + 1, dtype, sigma=2.0)
+    v = random_tensor((B, H, L, D), seed + 2, dtype)
+    scale = 1 / math.sqrt(D)
+    say(f"decode odd units B={B} H={H} L={L} splits={splits} D={D} dtype={dtype}")
+    m, d, op, o, lse = run_decode(q, k, v, scale, splits)
+    m_ref, d_ref, op_ref = oracle.decode_partials(q, k, v, scale, splits)
+    assert np.array_equal(np.isneginf(m), np.isneginf(m_ref))
+    ne = ~np.isneginf(m_ref)
+    assert np.max(np.abs(m[ne] - m_ref[ne])) <= 1e-3
+    f = np.exp(m[ne] - m_ref[ne])
+    assert np.max(np.abs(d[ne] * f - d_ref[ne]) / d_ref[ne]) <= 1e-3
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, False)
+    check(o, lse, o_ref.reshape(B * H, D), lse_ref.reshape(B * H), dtype,
+          f"decode odd units B={B} H={H} L={L} splits={splits}")
+
+
 def test_split_kv_decode_full_size():
     w = WORKLOADS["split_kv_decode"]
     say(f"workload {w.name}: drawing inputs")
