@@ -256,6 +256,9 @@ __global__ __launch_bounds__(256) void row_scan_kernel(const T* __restrict__ x, 
                                                      float* __restrict__ out1) {
   using S = typename M::S;
   __shared__ S wtot[4];
+  // A whole block's outputs go out through LDS so that every store instruction writes
+  // 1 KB of consecutive floats (a thread's own 8 results are 32 bytes apart per lane).
+  __shared__ __attribute__((aligned(16))) float stage[2][256 * kK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const T* p = x + row * int64_t(n);
@@ -313,7 +316,21 @@ __global__ __launch_bounds__(256) void row_scan_kernel(const T* __restrict__ x, 
       r0[i] = M::first(r);
       r1[i] = M::second(r);
     }
-    if (ALIGNED && e0 + kK <= n) {
+    if (ALIGNED && base + 256 * kK <= n) {  // uniform: the whole block is in the row
+#pragma unroll
+      for (int j = 0; j < kK; j += 4) {
+        *reinterpret_cast<f32x4_t*>(&stage[0][kK * tid + j]) = f32x4_t{r0[j], r0[j + 1], r0[j + 2], r0[j + 3]};
+        *reinterpret_cast<f32x4_t*>(&stage[1][kK * tid + j]) = f32x4_t{r1[j], r1[j + 1], r1[j + 2], r1[j + 3]};
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kK / 4; ++q) {
+        const int f = 4 * (tid + 256 * q);
+        *reinterpret_cast<f32x4_t*>(o0 + base + f) = *reinterpret_cast<const f32x4_t*>(&stage[0][f]);
+        *reinterpret_cast<f32x4_t*>(o1 + base + f) = *reinterpret_cast<const f32x4_t*>(&stage[1][f]);
+      }
+      // stage is rewritten by the next block only after that block's two barriers
+    } else if (ALIGNED && e0 + kK <= n) {
 #pragma unroll
       for (int j = 0; j < kK; j += 4) {
         *reinterpret_cast<f32x4_t*>(o0 + e0 + j) = f32x4_t{r0[j], r0[j + 1], r0[j + 2], r0[j + 3]};
