@@ -106,13 +106,67 @@ def _dense(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+# Validation of every tensor a C-named wrapper passes on. The library receives raw
+# pointers only, so a tensor of the wrong shape, dtype or device would otherwise be
+# read or written out of bounds on the GPU. Checks run in this order, before the
+# library is loaded: dtypes, shapes, contiguity, then that every tensor lives on one
+# CUDA device.
+def _want_dtype(name: str, t: torch.Tensor, dtype: torch.dtype) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _want_shape(name: str, t: torch.Tensor, shape: tuple) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_input_dtype(**ts) -> int:
+    """q, k, v (and dout) share one supported dtype; returns its FA_* code."""
+    items = list(ts.items())
+    code = _dtype_code(items[0][1])
+    for name, t in items[1:]:
+        if t.dtype != items[0][1].dtype:
+            raise TypeError(f"{name} must have the dtype of {items[0][0]} ({items[0][1].dtype}), "
+                            f"got {t.dtype}")
+    return code
+
+
+def _on_one_device(**ts) -> None:
+    dev = None
+    for name, t in ts.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA tensor, got device {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _checked(shapes: dict, f32: tuple, **ts) -> None:
+    """Shapes from `shapes` (name -> tuple), float32 for the names in `f32`, then
+    contiguity and one CUDA device for every tensor in ts."""
+    for name in f32:
+        _want_dtype(name, ts[name], torch.float32)
+    for name, shape in shapes.items():
+        _want_shape(name, ts[name], shape)
+    _dense(*ts.values())
+    _on_one_device(**ts)
+
+
 # ------------------------------------------------------------------ C-named calls
 def fa_forward(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     """q, k, v: [B, H, N, D] (bf16 or fp32, same dtype); o: [B, H, N, D] fp32; lse: [B, H, N] fp32."""
-    _dense(q, k, v, o, lse)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, D], got shape {tuple(q.shape)}")
     B, H, N, D = q.shape
+    dt = _same_input_dtype(q=q, k=k, v=v)
+    _checked({"k": q.shape, "v": q.shape, "o": q.shape, "lse": (B, H, N)}, ("o", "lse"),
+             q=q, k=k, v=v, o=o, lse=lse)
     code = load().fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
-                             float(scale), int(bool(causal)), _dtype_code(q), _stream(stream))
+                             float(scale), int(bool(causal)), dt, _stream(stream))
     _check(code, "fa_forward")
 
 
@@ -121,35 +175,57 @@ def fa_forward_ext(q, k, v, o, lse, scale: float, causal: bool, window_left: int
                    stream=None) -> None:
     """Dense: as fa_forward, plus the window. Packed (cu_seqlens, an int32 device tensor
     of nseq + 1 offsets): q, k, v, o [H, total, D], lse [H, total]."""
-    _dense(q, k, v, o, lse, cu_seqlens)
     if cu_seqlens is not None:
+        if q.dim() != 3:
+            raise ValueError(f"packed q must be [H, total, D], got shape {tuple(q.shape)}")
         if cu_seqlens.dtype != torch.int32:
             raise TypeError("cu_seqlens must be int32")
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D tensor of nseq + 1 offsets")
         H, N, D = q.shape
         B = cu_seqlens.numel() - 1
+        lse_shape = (H, N)
     else:
+        if q.dim() != 4:
+            raise ValueError(f"q must be [B, H, N, D], got shape {tuple(q.shape)}")
         B, H, N, D = q.shape
+        lse_shape = (B, H, N)
+    dt = _same_input_dtype(q=q, k=k, v=v)
+    _checked({"k": q.shape, "v": q.shape, "o": q.shape, "lse": lse_shape}, ("o", "lse"),
+             q=q, k=k, v=v, o=o, lse=lse, cu_seqlens=cu_seqlens)
     code = load().fa_forward_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, D,
                                  float(scale), int(bool(causal)), int(window_left),
                                  int(window_right), _ptr(cu_seqlens), int(max_seqlen),
-                                 _dtype_code(q), _stream(stream))
+                                 dt, _stream(stream))
     _check(code, "fa_forward_ext")
 
 
 def fa_decode_partials(q, k, v, m, d, o_part, scale: float, splits: int, stream=None) -> None:
     """q: [B, H, 1, D] or [B, H, D]; k, v: [B, H, L, D]; m, d: [B*H, splits]; o_part: [B*H, splits, D]."""
-    _dense(q, k, v, m, d, o_part)
+    if k.dim() != 4:
+        raise ValueError(f"k must be [B, H, L, D], got shape {tuple(k.shape)}")
     B, H, L, D = k.shape
+    splits = int(splits)
+    if splits < 1:
+        raise ValueError("splits must be >= 1")
+    if tuple(q.shape) not in ((B, H, 1, D), (B, H, D)):
+        raise ValueError(f"q must have shape {(B, H, 1, D)} or {(B, H, D)}, got {tuple(q.shape)}")
+    dt = _same_input_dtype(k=k, q=q, v=v)
+    _checked({"v": k.shape, "m": (B * H, splits), "d": (B * H, splits),
+              "o_part": (B * H, splits, D)}, ("m", "d", "o_part"),
+             q=q, k=k, v=v, m=m, d=d, o_part=o_part)
     code = load().fa_decode_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(d), _ptr(o_part),
-                                     B, H, L, D, float(scale), int(splits), _dtype_code(k),
-                                     _stream(stream))
+                                     B, H, L, D, float(scale), splits, dt, _stream(stream))
     _check(code, "fa_decode_partials")
 
 
 def fa_combine_partials(m, d, o_part, o, lse, stream=None) -> None:
     """m, d: [rows, splits] fp32; o_part: [rows, splits, D] fp32; o: [rows, D]; lse: [rows]."""
-    _dense(m, d, o_part, o, lse)
+    if o_part.dim() != 3:
+        raise ValueError(f"o_part must be [rows, splits, D], got shape {tuple(o_part.shape)}")
     rows, splits, D = o_part.shape
+    _checked({"m": (rows, splits), "d": (rows, splits), "o": (rows, D), "lse": (rows,)},
+             ("m", "d", "o_part", "o", "lse"), m=m, d=d, o_part=o_part, o=o, lse=lse)
     code = load().fa_combine_partials(_ptr(m), _ptr(d), _ptr(o_part), splits, rows, D,
                                       _ptr(o), _ptr(lse), _stream(stream))
     _check(code, "fa_combine_partials")
@@ -160,23 +236,31 @@ def fa_backward(q, k, v, o, lse, dout, delta, dq, dk, dv, scale: float, causal: 
     """q, k, v, dout: [B, H, N, D] (bf16 or fp32, same dtype); o: [B, H, N, D] fp32 and
     lse: [B, H, N] fp32 from fa_forward; delta: [B, H, N] fp32 scratch; dq, dk, dv:
     [B, H, N, D] fp32, written."""
-    _dense(q, k, v, o, lse, dout, delta, dq, dk, dv)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, D], got shape {tuple(q.shape)}")
     B, H, N, D = q.shape
-    if dout.dtype != q.dtype:
-        raise TypeError("dout must have the dtype of q, k and v")
+    dt = _same_input_dtype(q=q, k=k, v=v, dout=dout)
+    s = tuple(q.shape)
+    _checked({"k": s, "v": s, "dout": s, "o": s, "dq": s, "dk": s, "dv": s, "lse": (B, H, N),
+              "delta": (B, H, N)}, ("o", "lse", "delta", "dq", "dk", "dv"),
+             q=q, k=k, v=v, o=o, lse=lse, dout=dout, delta=delta, dq=dq, dk=dk, dv=dv)
     code = load().fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                               _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, D,
-                              float(scale), int(bool(causal)), _dtype_code(q), _stream(stream))
+                              float(scale), int(bool(causal)), dt, _stream(stream))
     _check(code, "fa_backward")
 
 
 def _rows(x, out0, out1):
-    _dense(x, out0, out1)
     if x.dim() < 1:
         raise ValueError("x needs at least one dimension (its rows are along the last)")
+    _dtype_code(x)
     n, rows = x.shape[-1], math.prod(x.shape[:-1])
-    if out0.numel() != rows or out1.numel() != rows:
-        raise ValueError(f"outputs must hold one value per row ({rows})")
+    for name, t in (("out0", out0), ("out1", out1)):
+        _want_dtype(name, t, torch.float32)
+        if t.numel() != rows:
+            raise ValueError(f"outputs must hold one value per row ({rows})")
+    _dense(x, out0, out1)
+    _on_one_device(x=x, out0=out0, out1=out1)
     return rows, n
 
 
@@ -197,11 +281,15 @@ def fa_moments(x, mean, m2, stream=None) -> None:
 
 
 def _scan_shapes(x, out0, out1):
-    _dense(x, out0, out1)
     if x.dim() < 1:
         raise ValueError("x needs at least one dimension (its rows are along the last)")
-    if out0.shape != x.shape or out1.shape != x.shape:
-        raise ValueError("scan outputs must have x's shape")
+    _dtype_code(x)
+    for name, t in (("out0", out0), ("out1", out1)):
+        _want_dtype(name, t, torch.float32)
+        if t.shape != x.shape:
+            raise ValueError("scan outputs must have x's shape")
+    _dense(x, out0, out1)
+    _on_one_device(x=x, out0=out0, out1=out1)
     return math.prod(x.shape[:-1]), x.shape[-1]
 
 
@@ -224,9 +312,10 @@ def fa_moments_scan(x, mean, m2, stream=None) -> None:
 def fa_calibrate_mfma(out, blocks: int, iters: int, seed: int = 0, stream=None) -> None:
     """Measurement only: the MFMA-only loop; out: fp32 [blocks * 512] (checksums).
     One launch is 2**19 * 8 * blocks * iters flops."""
-    _dense(out)
     if out.dtype != torch.float32 or out.numel() != blocks * 512:
         raise ValueError("out must be float32 with blocks * 512 elements")
+    _dense(out)
+    _on_one_device(out=out)
     code = load().fa_calibrate_mfma(_ptr(out), int(blocks), int(iters), int(seed) & 0xFFFFFFFF,
                                     _stream(stream))
     _check(code, "fa_calibrate_mfma")
@@ -235,9 +324,10 @@ def fa_calibrate_mfma(out, blocks: int, iters: int, seed: int = 0, stream=None) 
 def fa_calibrate_read(x, out, blocks: int, stream=None) -> None:
     """Measurement only: a read-only stream over the bytes of x (a multiple of 16);
     out: int32 [blocks * 256], each thread's XOR of the 32-bit words it read."""
-    _dense(x, out)
     if out.dtype != torch.int32 or out.numel() != blocks * 256:
         raise ValueError("out must be int32 with blocks * 256 elements")
+    _dense(x, out)
+    _on_one_device(x=x, out=out)
     nbytes = x.numel() * x.element_size()
     code = load().fa_calibrate_read(_ptr(x), nbytes, _ptr(out), int(blocks), _stream(stream))
     _check(code, "fa_calibrate_read")
@@ -247,6 +337,7 @@ def fa_calibrate_write(y, value: int, blocks: int, stream=None) -> None:
     """Measurement only: a write-only stream over the bytes of y (a multiple of 16);
     16-byte word w becomes {value, w, value, w} as 32-bit words."""
     _dense(y)
+    _on_one_device(y=y)
     nbytes = y.numel() * y.element_size()
     code = load().fa_calibrate_write(_ptr(y), nbytes, int(value) & 0xFFFFFFFF, int(blocks),
                                      _stream(stream))

@@ -52,9 +52,10 @@ enum {
   FA_ERR_ALIGN = -4, /* a tensor pointer is not 16-byte aligned; m, d, lse or delta
                         not 4-byte aligned; a row-reduction input not aligned to its
                         element                                                     */
-  FA_ERR_ARG = -5,   /* scale not finite or not > 0, causal not 0 or 1, or a window
-                        bound below -1                                              */
-  FA_ERR_HIP = -6    /* the HIP runtime rejected the kernel launch                   */
+  FA_ERR_HIP = -5,   /* the HIP runtime rejected the kernel launch                   */
+  FA_ERR_ARG = -6    /* scale not finite or not > 0, causal not 0 or 1, or a window
+                        bound below -1 (numbered after FA_ERR_HIP so the first five
+                        codes keep the values of the original five-code interface) */
 };
 
 /*

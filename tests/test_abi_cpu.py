@@ -16,7 +16,7 @@ from exact_io_aware_22_amd import fa
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "fa.h"
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ARG = 0, -1, -2, -3, -4, -5
+OK, NULL, SHAPE, DTYPE, ALIGN, HIP, ARG = 0, -1, -2, -3, -4, -5, -6
 P = 1 << 20  # a fake, 16-byte-aligned, never dereferenced address
 
 
@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_strerror(lib):
     assert lib.fa_abi_version() == 1
-    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, ARG, -6, 12345):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, HIP, ARG, 12345):
         msg = fa.strerror(code)
         assert isinstance(msg, str) and msg
 
