@@ -72,6 +72,7 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+CPU_SHARE = 16  # host cores one GPU's jobs may use on a shared host
 WARM_SECONDS = 0.25  # the clock ramps up over the first tens of milliseconds of load
 
 
@@ -245,7 +246,81 @@ def bench_decode(steps: int, warmup: int, torch, fa, make_inputs, W):
                      "read_bytes": part_bytes, "write_bytes": BH * S * (D + 2) * 4},
     }
     del qd, kd, vd
+    torch.cuda.empty_cache()
+    res["one_gpu_share"] = bench_decode_share(steps, warmup, torch, fa, q, k, v, w)
     return res
+
+
+def bench_decode_share(steps: int, warmup: int, torch, fa, q, k, v, w, shards: int = 8):
+    """What one GPU of an 8-GPU split-KV decode does: fa_decode_partials over its share of
+    the keys (L / 8 = 4096 per head, B=16, H=32) in 8 and in 64 chunks, and the merge of
+    all 8 shards' 64 partials each (rows = 512, 512 partials per row) by one
+    fa_combine_partials call, as after an all-gather of the partials."""
+    per = w.L // shards
+    qd = q.cuda()
+    ks = k[:, :, :per].contiguous().cuda()
+    vs = v[:, :, :per].contiguous().cuda()
+    BH, D = w.B * w.H, w.D
+    out = {"keys_per_head": per, "shards": shards, "partials": []}
+    kv_bytes = 2 * BH * per * D * 2 + BH * D * 2
+    for splits in (8, 64):
+        m = torch.empty(BH, splits, device="cuda")
+        d = torch.empty(BH, splits, device="cuda")
+        op = torch.empty(BH, splits, D, device="cuda")
+        ms = time_launches(lambda: fa.fa_decode_partials(qd, ks, vs, m, d, op, w.scale, splits),
+                           steps, warmup, torch)
+        gbs = kv_bytes / (ms * 1e-3) / 1e9
+        out["partials"].append({"splits": splits, "ms": ms, "gbs": gbs,
+                                "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+                                "algorithmic_bytes": kv_bytes})
+        del m, d, op
+    P = shards * w.splits
+    m = torch.empty(BH, P, device="cuda")
+    d = torch.empty(BH, P, device="cuda")
+    op = torch.empty(BH, P, D, device="cuda")
+    for s in range(shards):  # each shard's partials, as its GPU would have produced them
+        ksl = k[:, :, s * per:(s + 1) * per].contiguous().cuda()
+        vsl = v[:, :, s * per:(s + 1) * per].contiguous().cuda()
+        mp, dp = torch.empty(BH, w.splits, device="cuda"), torch.empty(BH, w.splits, device="cuda")
+        opp = torch.empty(BH, w.splits, D, device="cuda")
+        fa.fa_decode_partials(qd, ksl, vsl, mp, dp, opp, w.scale, w.splits)
+        m.view(BH, shards, w.splits)[:, s] = mp
+        d.view(BH, shards, w.splits)[:, s] = dp
+        op.view(BH, shards, w.splits, D)[:, s] = opp
+        del ksl, vsl, mp, dp, opp
+    o = torch.empty(BH, D, device="cuda")
+    lse = torch.empty(BH, device="cuda")
+    ms = time_launches(lambda: fa.fa_combine_partials(m, d, op, o, lse), steps, warmup, torch)
+    comb_bytes = BH * P * (D + 2) * 4 + BH * (D + 1) * 4
+    out["combine_remote"] = {"rows": BH, "partials_per_row": P, "ms": ms,
+                             "gbs": comb_bytes / (ms * 1e-3) / 1e9,
+                             "algorithmic_bytes": comb_bytes}
+    del qd, ks, vs, m, d, op, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_overlap(torch, fa, blocks: int = 256, iters: int = 4096):
+    """fa_calibrate_overlap: milliseconds of each mode (one workgroup of 8 wavefronts per
+    CU) and the share of the shorter role's time that runs concurrently with the other
+    when one matrix and one vector wavefront share each SIMD:
+    (t_matrix + t_vector - t_both) / min(t_matrix, t_vector); 1 = full overlap, 0 = none."""
+    out_buf = torch.empty(blocks * 512, device="cuda")
+    fa.fa_calibrate_overlap(out_buf, blocks, 0, 6)
+    torch.cuda.synchronize()
+    simd = out_buf.view(blocks, 8, 64)[:, :, 0].cpu()
+    paired = bool(torch.equal(simd[:, :4], simd[:, 4:]))
+    names = ["matrix_1_per_simd", "vector_1_per_simd", "matrix_and_vector_per_simd",
+             "both_roles_every_wave", "matrix_2_per_simd", "vector_2_per_simd"]
+    ms = {}
+    for mode, name in enumerate(names):
+        ms[name] = time_launches(lambda: fa.fa_calibrate_overlap(out_buf, blocks, iters, mode),
+                                 5, 3, torch)
+    t0, t1, t2 = ms[names[0]], ms[names[1]], ms[names[2]]
+    return {"blocks": blocks, "iters": iters, "ms": ms,
+            "waves_w_and_w_plus_4_share_a_simd": paired,
+            "overlap_fraction": (t0 + t1 - t2) / min(t0, t1),
+            "matrix_tflops_1_per_simd": 2 ** 15 * 16 * 4 * blocks * iters / (t0 * 1e-3) / 1e12}
 
 
 def cpu_baseline(q, k, v, w, budget_s: float):
@@ -256,7 +331,10 @@ def cpu_baseline(q, k, v, w, budget_s: float):
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    host_cpus = len(os.sched_getaffinity(0))
+    # The host is shared by the GPUs of its node and one GPU's jobs get 16 of its cores,
+    # so the oracle takes every core this process may use, up to that share.
+    cores = max(1, min(CPU_SHARE, host_cpus))
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     heads, t_used = 0, 0.0
     try:
@@ -277,18 +355,31 @@ def cpu_baseline(q, k, v, w, budget_s: float):
         if ctx:
             ctx.__exit__(None, None, None)
     flops = w.flops() / (w.B * w.H) * heads
-    cpu = "unknown"
-    try:
-        for line in Path("/proc/cpuinfo").read_text().splitlines():
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} heads of {w.name} (all {w.N} rows each), fp64 numpy, "
                       f"BLAS 1 thread per worker",
-            "seconds": t_used, "cpu_model": cpu}
+            "seconds": t_used, "host_cpus_visible": host_cpus, "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: its model-name line, with the vendor,
+    family, model and stepping fields (a virtualised host may give a short name)."""
+    fields = {}
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if ":" not in line:
+                if fields:
+                    break  # the first processor's block is enough
+                continue
+            key, val = (s.strip() for s in line.split(":", 1))
+            if key in ("model name", "vendor_id", "cpu family", "model", "stepping"):
+                fields.setdefault(key, val)
+    except OSError:
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    extra = ", ".join(f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model", "stepping")
+                      if k in fields)
+    return f"{name} ({extra})" if extra else name
 
 
 def bench_backward(steps: int, warmup: int, torch, fa, make_inputs, W):
@@ -422,7 +513,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "masks",
-                                       "reductions", "copy", "ceilings"],
+                                       "reductions", "copy", "ceilings", "overlap"],
                     default="all")
     ap.add_argument("--workload", default=HEADLINE, choices=[HEADLINE] + EXTRA,
                     help="with --only prefill: the prefill workload to time (default: the "
@@ -453,7 +544,11 @@ def main() -> int:
         copy_calibration(torch, 1 << 30, args.steps)
         return 0
     if args.only == "ceilings":
-        print(json.dumps({"ceilings": measured_ceilings(args.steps, args.warmup, torch, fa)}))
+        print(json.dumps({"ceilings": measured_ceilings(args.steps, args.warmup, torch, fa),
+                          "overlap": measure_overlap(torch, fa)}))
+        return 0
+    if args.only == "overlap":
+        print(json.dumps({"overlap": measure_overlap(torch, fa)}))
         return 0
 
     out = {"metric": METRIC}
@@ -519,6 +614,7 @@ def main() -> int:
         # Measured last, so the headline is not timed on a clock the GEMM has heated.
         log("timing the measured ceilings (MFMA-only loop, read and write streams, library references)")
         ceil = measured_ceilings(10, 5, torch, fa)
+        ceil["overlap"] = measure_overlap(torch, fa)
         out["ceilings"] = ceil
         mfma_rooflines = [out.get("roofline"), out.get("backward", {}).get("roofline")]
         for r in mfma_rooflines:

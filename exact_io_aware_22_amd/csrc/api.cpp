@@ -205,6 +205,15 @@ int fa_calibrate_mfma(float* out, int blocks, int iters, unsigned seed, void* st
       fa::launch_calibrate_mfma(out, blocks, iters, seed, static_cast<hipStream_t>(stream)));
 }
 
+int fa_calibrate_overlap(float* out, int blocks, int iters, int mode, void* stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 0) return FA_ERR_SHAPE;
+  if (mode < 0 || mode > 6) return FA_ERR_ARG;
+  if (!out) return FA_ERR_NULL;
+  if (!aligned(out, 4)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_calibrate_overlap(out, blocks, iters, mode,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks,
                       void* stream) {
   if (blocks < 1 || blocks > (1 << 22) || nbytes < 0 || nbytes % 16 != 0) return FA_ERR_SHAPE;

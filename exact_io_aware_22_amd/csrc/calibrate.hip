@@ -69,6 +69,104 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(float* __restri
   out[gid] = s;
 }
 
+// Overlap probe: does one SIMD run a matrix-product wavefront and a vector-ALU wavefront
+// at the same time? One workgroup of 8 wavefronts per CU (the launch asks for more than
+// half of the CU's LDS), so each SIMD holds wavefronts w and w + 4. Per round, the
+// matrix role issues the prefill step's 16 products (one dependent chain of 8 into the
+// score tile and 4 chains of 2 into output tiles, as QK^T and PV of a 32-key block);
+// the vector role issues the step's softmax instruction mix (16 FMA, 16 exp2, 15 adds,
+// 8 bf16 packs and 8 bf16 dot products), made loop-carried so nothing is hoisted.
+//   mode 0: wavefronts 0-3 matrix role, 4-7 leave   (one matrix wavefront per SIMD)
+//   mode 1: wavefronts 4-7 vector role, 0-3 leave   (one vector wavefront per SIMD)
+//   mode 2: wavefronts 0-3 matrix, 4-7 vector       (one of each per SIMD)
+//   mode 3: every wavefront both roles, interleaved in one instruction stream
+//   mode 4: every wavefront the matrix role          (two matrix wavefronts per SIMD)
+//   mode 5: every wavefront the vector role          (two vector wavefronts per SIMD)
+//   mode 6: placement: each thread writes its wavefront's SIMD index (HW_ID bits 5:4)
+// Every loop runs exactly `iters` rounds and every wavefront exits normally.
+constexpr int kOverlapLds = 96 * 1024;
+
+__device__ __forceinline__ void overlap_matrix_round(const u32x4_t (&a)[8], const u32x4_t (&b)[8],
+                                                     f32x16_t& sacc, f32x16_t (&oacc)[4]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[i]), sacc, 0, 0, 0);
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[(4 * cc + db + 3) & 7]),
+                                                         as_bf16x8(b[(2 * db + cc + 5) & 7]),
+                                                         oacc[db], 0, 0, 0);
+}
+
+__device__ __forceinline__ void overlap_vector_round(const float (&s)[16], float c, float& nmc,
+                                                     float& ps_acc, float& pq) {
+  const bf16x2_t ones = as_bf16x2(0x3f803f80u);
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p0 = exp2_hw(fmaf(s[2 * i], c, nmc));
+    const float p1 = exp2_hw(fmaf(s[2 * i + 1], c, nmc));
+    ps = i == 0 ? p0 + p1 : ps + (p0 + p1);
+    const uint32_t pk = pack_bf16x2(p0, p1);
+    pq = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pk), ones, pq, false);
+  }
+  ps_acc += ps;
+  nmc = fmaf(pq, -1e-30f, nmc);  // carries the round into the next one's exponents
+}
+
+__global__ __launch_bounds__(kMfmaThreads) void overlap_kernel(float* __restrict__ out,
+                                                               int iters, int mode) {
+  extern __shared__ uint8_t overlap_lds[];  // reserved only, to hold one workgroup per CU
+  const uint32_t gid = blockIdx.x * kMfmaThreads + threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  if (mode == 6) {
+    // HW_ID (hardware register 4), bits 5:4: the SIMD this wavefront runs on.
+    const int simd = __builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11));
+    out[gid] = float(simd);
+    return;
+  }
+  const bool matrix = mode == 3 || mode == 4 || (wave < 4 && (mode == 0 || mode == 2));
+  const bool vector = mode == 3 || mode == 5 || (wave >= 4 && (mode == 1 || mode == 2));
+  if (!matrix && !vector) {
+    out[gid] = 0.f;
+    return;
+  }
+  const uint32_t sa = mix32(0x1234567u), sb = mix32(0x89abcdefu);
+  u32x4_t a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[i][j] = rand_bf16x2(mix32(sa ^ (gid * 64u + 8u * i + j)));
+      b[i][j] = rand_bf16x2(mix32(sb ^ (gid * 64u + 8u * i + j)));
+    }
+  float s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = float(int(mix32(gid * 16u + i) & 1023u) - 512) * 0.03f;
+  f32x16_t sacc = {}, oacc[4] = {};
+  float nmc = -4.0f, ps_acc = 0.f, pq = 0.f;
+  const float c = 0.1275f;
+  if (matrix && vector) {
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) {
+      overlap_matrix_round(a, b, sacc, oacc);
+      overlap_vector_round(s, c, nmc, ps_acc, pq);
+    }
+  } else if (matrix) {
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) overlap_matrix_round(a, b, sacc, oacc);
+  } else {
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it) overlap_vector_round(s, c, nmc, ps_acc, pq);
+  }
+  float r = ps_acc + pq;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) r += sacc[k] + oacc[0][k] + oacc[1][k] + oacc[2][k] + oacc[3][k];
+  out[gid] = r;
+}
+
 // Workgroup b reads the 16-byte words [b span, min(n16, (b + 1) span)), thread t those at
 // positions t mod 256 of the span, eight loads in flight.
 __global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4_t* __restrict__ x,
@@ -118,6 +216,13 @@ hipError_t launch_calibrate_mfma(float* out, int blocks, int iters, uint32_t see
                                  hipStream_t s) {
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(unsigned(blocks)), dim3(kMfmaThreads), 0, s, out,
                      iters, seed);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate_overlap(float* out, int blocks, int iters, int mode,
+                                    hipStream_t s) {
+  hipLaunchKernelGGL(overlap_kernel, dim3(unsigned(blocks)), dim3(kMfmaThreads), kOverlapLds, s,
+                     out, iters, mode);
   return hipGetLastError();
 }
 

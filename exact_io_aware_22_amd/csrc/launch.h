@@ -81,6 +81,8 @@ hipError_t launch_softmax_scan(const RowReduceArgs& a, hipStream_t s);
 hipError_t launch_moments_scan(const RowReduceArgs& a, hipStream_t s);
 
 hipError_t launch_calibrate_mfma(float* out, int blocks, int iters, uint32_t seed, hipStream_t s);
+hipError_t launch_calibrate_overlap(float* out, int blocks, int iters, int mode,
+                                    hipStream_t s);
 hipError_t launch_calibrate_read(const void* x, int64_t nbytes, uint32_t* out, int blocks,
                                  hipStream_t s);
 hipError_t launch_calibrate_write(void* y, int64_t nbytes, uint32_t value, int blocks,

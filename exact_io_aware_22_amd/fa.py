@@ -25,7 +25,7 @@ FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
             "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-            "fa_calibrate_mfma", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
+            "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
             "fa_abi_version")
 
 
@@ -63,6 +63,8 @@ def load():
     lib.fa_backward.restype = i
     lib.fa_calibrate_mfma.argtypes = [vp, i, i, ctypes.c_uint, vp]
     lib.fa_calibrate_mfma.restype = i
+    lib.fa_calibrate_overlap.argtypes = [vp, i, i, i, vp]
+    lib.fa_calibrate_overlap.restype = i
     lib.fa_calibrate_read.argtypes = [vp, ctypes.c_longlong, vp, i, vp]
     lib.fa_calibrate_read.restype = i
     lib.fa_calibrate_write.argtypes = [vp, ctypes.c_longlong, ctypes.c_uint, i, vp]
@@ -319,6 +321,18 @@ def fa_calibrate_mfma(out, blocks: int, iters: int, seed: int = 0, stream=None) 
     code = load().fa_calibrate_mfma(_ptr(out), int(blocks), int(iters), int(seed) & 0xFFFFFFFF,
                                     _stream(stream))
     _check(code, "fa_calibrate_mfma")
+
+
+def fa_calibrate_overlap(out, blocks: int, iters: int, mode: int, stream=None) -> None:
+    """Measurement only: the matrix/vector overlap probe (modes 0-6, see include/fa.h);
+    out: fp32 [blocks * 512] (checksums, or SIMD indices in mode 6)."""
+    if out.dtype != torch.float32 or out.numel() != blocks * 512:
+        raise ValueError("out must be float32 with blocks * 512 elements")
+    _dense(out)
+    _on_one_device(out=out)
+    code = load().fa_calibrate_overlap(_ptr(out), int(blocks), int(iters), int(mode),
+                                       _stream(stream))
+    _check(code, "fa_calibrate_overlap")
 
 
 def fa_calibrate_read(x, out, blocks: int, stream=None) -> None:

@@ -239,6 +239,23 @@ int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int 
  *   x 16-byte aligned (may be NULL only when nbytes = 0), out 4-byte aligned.
  */
 int fa_calibrate_mfma(float* out, int blocks, int iters, unsigned seed, void* stream);
+/*
+ * fa_calibrate_overlap -- whether one SIMD overlaps a matrix-product wavefront with a
+ * vector-ALU wavefront. `blocks` workgroups of 8 wavefronts, one per CU (each reserves
+ * 96 KB of LDS), so wavefronts w and w + 4 share a SIMD. Per round the matrix role
+ * issues 16 bf16 products 32x32x16 in the pattern of one 32-key prefill step (a chain
+ * of 8 and four chains of 2); the vector role issues that step's softmax instructions
+ * (16 FMA, 16 exp2, 15 adds, 8 bf16 packs, 8 bf16 dot products).
+ *   mode 0: wavefronts 0-3 matrix role only; 1: wavefronts 4-7 vector role only;
+ *   2: both at once (one of each per SIMD); 3: every wavefront both roles in one
+ *   instruction stream; 4: every wavefront the matrix role; 5: every wavefront the
+ *   vector role; 6: each thread writes its wavefront's SIMD index (placement check).
+ *   Each role runs exactly `iters` rounds.
+ *   out : [blocks * 512] float32, written: each thread's checksum (mode 6: SIMD index;
+ *         0 for a wavefront with no role).
+ *   1 <= blocks <= 2^20, iters >= 0 (FA_ERR_SHAPE); mode in 0..6 (FA_ERR_ARG).
+ */
+int fa_calibrate_overlap(float* out, int blocks, int iters, int mode, void* stream);
 int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks, void* stream);
 /*
  * fa_calibrate_write -- a write-only stream over y[0 .. nbytes) in 16-byte non-temporal

@@ -37,7 +37,7 @@ def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
          "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-         "fa_calibrate_mfma", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
+         "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
          "fa_abi_version"])
 
 
@@ -229,4 +229,5 @@ def test_calibration_validation(lib):
     assert wr(P, 1000, 1, 4, None) == SHAPE
     assert wr(P, 1024, 1, 0, None) == SHAPE
     assert wr(P + 8, 1024, 1, 4, None) == ALIGN
+
 

@@ -74,3 +74,35 @@ def test_write_stream_pattern(n16, blocks):
                      np.full(n16, 0x5EED1234, np.uint32), w], axis=1).reshape(-1)
     assert np.array_equal(got[:4 * n16], want)
     assert not got[4 * n16:].any()  # nothing past the end
+
+
+def test_overlap_probe_placement_and_checksums():
+    """fa_calibrate_overlap: one workgroup of 8 wavefronts per CU, wavefronts w and w + 4
+    on one SIMD (so mode 2 pairs one matrix with one vector wavefront per SIMD); every
+    mode ends with finite checksums, and a wavefront with no role writes 0."""
+    blocks = 64
+    out = torch.full((blocks * 512,), float("nan"), device="cuda")
+    fa.fa_calibrate_overlap(out, blocks, 0, 6)
+    torch.cuda.synchronize()
+    simd = out.view(blocks, 8, 64).cpu()
+    assert torch.all(simd == simd[:, :, :1]), "one SIMD per wavefront"
+    s = simd[:, :, 0]
+    assert set(s.unique().tolist()) <= {0.0, 1.0, 2.0, 3.0}
+    assert torch.equal(s[:, :4], s[:, 4:]), "wavefronts w and w + 4 share a SIMD"
+    assert all(sorted(row[:4].tolist()) == [0.0, 1.0, 2.0, 3.0] for row in s)
+    for mode in range(6):
+        out.fill_(float("nan"))
+        fa.fa_calibrate_overlap(out, blocks, 3, mode)
+        torch.cuda.synchronize()
+        w = out.view(blocks, 8, 64).cpu()
+        assert torch.all(torch.isfinite(w)), f"mode {mode}"
+        if mode == 0:
+            assert torch.all(w[:, 4:] == 0)
+        if mode == 1:
+            assert torch.all(w[:, :4] == 0)
+
+
+def test_overlap_probe_rejects_bad_mode():
+    out = torch.empty(512, device="cuda")
+    with pytest.raises(fa.FaError):
+        fa.fa_calibrate_overlap(out, 1, 1, 7)

@@ -20,6 +20,7 @@ import pytest
 import torch
 
 import oracle
+from tests.conftest import parallel_map
 from exact_io_aware_22_amd import fa
 from exact_io_aware_22_amd.workloads import random_tensor
 
@@ -125,11 +126,13 @@ def test_scans_end_in_the_reductions():
     np.testing.assert_allclose(m2[:, -1], m2r.cpu().double().numpy(), rtol=1e-4)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["moments_activations_bf16", "softmax_stats_logits_fp32"])
-def test_scan_full_size_sampled_prefixes(name):
-    """The benchmark's scans at full size (the row reductions' 1 GiB inputs); 18 sampled
-    (row, position) states, each against the oracle's reduction of that prefix, within
-    the tolerances above."""
+def test_scan_full_size_whole_rows(name):
+    """The benchmark's scans at full size (the row reductions' 1 GiB inputs): every
+    position of 6 whole rows (the first, the last and 4 seeded ones) against the
+    oracle's reduction of each prefix, within the tolerances above; every row's last
+    position against the oracle's reduction of the whole row."""
     from exact_io_aware_22_amd.workloads import ROW_WORKLOADS, make_rows
 
     w = ROW_WORKLOADS[name]
@@ -141,20 +144,32 @@ def test_scan_full_size_sampled_prefixes(name):
     say(f"{name} scan at full size")
     (fa.fa_softmax_scan if softmax else fa.fa_moments_scan)(xd, a, b)
     torch.cuda.synchronize()
+    del xd
     rng = np.random.default_rng(6)
-    pairs = [(int(rng.integers(w.rows)), int(rng.integers(w.n))) for _ in range(16)]
-    pairs += [(0, 0), (w.rows - 1, w.n - 1)]
-    k = w.n / 2048 + 32
-    for r, j in pairs:
-        pref = x[r:r + 1, :j + 1]
-        ga, gb = float(a[r, j]), float(b[r, j])
-        if softmax:
-            m_ref, d_ref = oracle.softmax_stats(pref)
-            assert ga == m_ref[0], f"{name}: m at ({r}, {j})"
-            assert abs(gb - d_ref[0]) <= k * 4 * U * d_ref[0], f"{name}: d at ({r}, {j})"
-        else:
-            _, mu_ref, m2_ref = oracle.moments(pref)
-            xa = float(pref.double().abs().max())
-            assert abs(ga - mu_ref[0]) <= k * 4 * U * xa, f"{name}: mean at ({r}, {j})"
-            assert abs(gb - m2_ref[0]) <= k * 8 * U * (j + 1) * xa ** 2, f"{name}: M2 at ({r}, {j})"
+    rows = sorted({0, w.rows - 1, *(int(r) for r in rng.choice(w.rows, 4, replace=False))})
+    ga = a[rows].cpu().double().numpy()
+    gb = b[rows].cpu().double().numpy()
+    last_a = a[:, -1].cpu().double().numpy()
+    last_b = b[:, -1].cpu().double().numpy()
+    del a, b
+    torch.cuda.empty_cache()
 
+    def whole_row(i):
+        r = rows[i]
+        sub = x[r:r + 1]
+        if softmax:
+            check_softmax_scan(sub, ga[i:i + 1], gb[i:i + 1], f"{name} row {r} (all {w.n})")
+        else:
+            check_moments_scan(sub, ga[i:i + 1], gb[i:i + 1], f"{name} row {r} (all {w.n})")
+
+    parallel_map(whole_row, range(len(rows)))
+    k = w.n / 2048 + 32
+    if softmax:
+        m_ref, d_ref = oracle.softmax_stats(x)
+        assert np.array_equal(last_a, m_ref)
+        assert np.all(np.abs(last_b - d_ref) <= k * 4 * U * d_ref)
+    else:
+        _, mu_ref, m2_ref = oracle.moments(x)
+        xa = x.abs().amax(dim=1).double().numpy()
+        assert np.all(np.abs(last_a - mu_ref) <= k * 4 * U * xa)
+        assert np.all(np.abs(last_b - m2_ref) <= k * 8 * U * w.n * xa ** 2)

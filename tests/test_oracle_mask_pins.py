@@ -128,3 +128,20 @@ def test_varlen_sequences_are_independent_and_permutable():
     o2, l2 = oracle.attention_varlen(q[:, idx], k[:, idx], v[:, idx], cu2, 0.5, True)
     np.testing.assert_allclose(o2, o[:, idx], atol=1e-14)
     np.testing.assert_allclose(l2, lse[:, idx], atol=1e-14)
+
+
+def test_window_row_block_and_workers_do_not_matter():
+    """The thread pool and the row blocking are plumbing: any split of the independent
+    (b, h, row-block) units gives the same rows (up to the BLAS's own blocking)."""
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((2, 3, 75, 8)) for _ in range(3))
+    for causal, wl, wr in ((True, 10, -1), (False, 7, 3), (False, -1, -1)):
+        o1, l1 = oracle.attention_window(q, k, v, 0.4, causal, wl, wr, row_block=1024)
+        o2, l2 = oracle.attention_window(q, k, v, 0.4, causal, wl, wr, row_block=7, workers=5)
+        np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
+    cu = np.array([0, 20, 21, 75])
+    o1, l1 = oracle.attention_varlen(q[0], k[0], v[0], cu, 0.4, True)
+    o2, l2 = oracle.attention_varlen(q[0], k[0], v[0], cu, 0.4, True, workers=3)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-13)
