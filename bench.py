@@ -317,7 +317,16 @@ def measure_overlap(torch, fa, blocks: int = 256, iters: int = 4096):
         ms[name] = time_launches(lambda: fa.fa_calibrate_overlap(out_buf, blocks, iters, mode),
                                  5, 3, torch)
     t0, t1, t2 = ms[names[0]], ms[names[1]], ms[names[2]]
-    return {"blocks": blocks, "iters": iters, "ms": ms,
+    clock = {}
+    for mode, name in enumerate(names):  # the shader clock each mode ran at
+        out_buf.zero_()
+        fa.fa_calibrate_overlap(out_buf, blocks, iters, 8 + mode)
+        torch.cuda.synchronize()
+        t = out_buf.view(blocks, 8, 64).cpu()
+        cyc, ticks = t[:, :, 0].flatten(), t[:, :, 32].flatten()
+        live = ticks > 0
+        clock[name] = float((cyc[live] / ticks[live]).median()) * 100.0  # MHz
+    return {"blocks": blocks, "iters": iters, "ms": ms, "clock_mhz": clock,
             "waves_w_and_w_plus_4_share_a_simd": paired,
             "overlap_fraction": (t0 + t1 - t2) / min(t0, t1),
             "matrix_tflops_1_per_simd": 2 ** 15 * 16 * 4 * blocks * iters / (t0 * 1e-3) / 1e12}

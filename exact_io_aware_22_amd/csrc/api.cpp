@@ -207,7 +207,7 @@ int fa_calibrate_mfma(float* out, int blocks, int iters, unsigned seed, void* st
 
 int fa_calibrate_overlap(float* out, int blocks, int iters, int mode, void* stream) {
   if (blocks < 1 || blocks > (1 << 20) || iters < 0) return FA_ERR_SHAPE;
-  if (mode < 0 || mode > 6) return FA_ERR_ARG;
+  if (mode < 0 || mode > 13 || mode == 7) return FA_ERR_ARG;
   if (!out) return FA_ERR_NULL;
   if (!aligned(out, 4)) return FA_ERR_ALIGN;
   return hip_status(fa::launch_calibrate_overlap(out, blocks, iters, mode,

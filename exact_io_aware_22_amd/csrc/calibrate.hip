@@ -83,6 +83,10 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_loop_kernel(float* __restri
 //   mode 4: every wavefront the matrix role          (two matrix wavefronts per SIMD)
 //   mode 5: every wavefront the vector role          (two vector wavefronts per SIMD)
 //   mode 6: placement: each thread writes its wavefront's SIMD index (HW_ID bits 5:4)
+//   mode 8 + m (m = 0..5): mode m, timed: instead of its checksum each thread of a
+//           wavefront with a role writes that wavefront's elapsed shader-clock cycles
+//           (s_memtime, lanes 0-31) or elapsed 100 MHz real-time ticks (s_memrealtime,
+//           lanes 32-63) over its loop, so the clock each mode ran at can be read off.
 // Every loop runs exactly `iters` rounds and every wavefront exits normally.
 constexpr int kOverlapLds = 96 * 1024;
 
@@ -127,8 +131,10 @@ __global__ __launch_bounds__(kMfmaThreads) void overlap_kernel(float* __restrict
     out[gid] = float(simd);
     return;
   }
-  const bool matrix = mode == 3 || mode == 4 || (wave < 4 && (mode == 0 || mode == 2));
-  const bool vector = mode == 3 || mode == 5 || (wave >= 4 && (mode == 1 || mode == 2));
+  const bool timed = mode >= 8;
+  const int m = mode & 7;
+  const bool matrix = m == 3 || m == 4 || (wave < 4 && (m == 0 || m == 2));
+  const bool vector = m == 3 || m == 5 || (wave >= 4 && (m == 1 || m == 2));
   if (!matrix && !vector) {
     out[gid] = 0.f;
     return;
@@ -148,6 +154,11 @@ __global__ __launch_bounds__(kMfmaThreads) void overlap_kernel(float* __restrict
   f32x16_t sacc = {}, oacc[4] = {};
   float nmc = -4.0f, ps_acc = 0.f, pq = 0.f;
   const float c = 0.1275f;
+  uint64_t c0 = 0, r0 = 0;
+  if (timed) {
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   if (matrix && vector) {
 #pragma unroll 1
     for (int it = 0; it < iters; ++it) {
@@ -164,7 +175,13 @@ __global__ __launch_bounds__(kMfmaThreads) void overlap_kernel(float* __restrict
   float r = ps_acc + pq;
 #pragma unroll
   for (int k = 0; k < 16; ++k) r += sacc[k] + oacc[0][k] + oacc[1][k] + oacc[2][k] + oacc[3][k];
-  out[gid] = r;
+  if (timed) {
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    const float ticks = (threadIdx.x & 63) < 32 ? float(c1 - c0) : float(r1 - r0);
+    out[gid] = ticks + (r == 1.2345e30f ? 1.f : 0.f);  // keeps the checksum's work alive
+  } else {
+    out[gid] = r;
+  }
 }
 
 // Workgroup b reads the 16-byte words [b span, min(n16, (b + 1) span)), thread t those at

@@ -324,8 +324,9 @@ def fa_calibrate_mfma(out, blocks: int, iters: int, seed: int = 0, stream=None) 
 
 
 def fa_calibrate_overlap(out, blocks: int, iters: int, mode: int, stream=None) -> None:
-    """Measurement only: the matrix/vector overlap probe (modes 0-6, see include/fa.h);
-    out: fp32 [blocks * 512] (checksums, or SIMD indices in mode 6)."""
+    """Measurement only: the matrix/vector overlap probe (modes 0-6 and 8-13, see
+    include/fa.h); out: fp32 [blocks * 512] (checksums, SIMD indices in mode 6, elapsed
+    cycles / real-time ticks in modes 8-13)."""
     if out.dtype != torch.float32 or out.numel() != blocks * 512:
         raise ValueError("out must be float32 with blocks * 512 elements")
     _dense(out)

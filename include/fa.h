@@ -249,11 +249,13 @@ int fa_calibrate_mfma(float* out, int blocks, int iters, unsigned seed, void* st
  *   mode 0: wavefronts 0-3 matrix role only; 1: wavefronts 4-7 vector role only;
  *   2: both at once (one of each per SIMD); 3: every wavefront both roles in one
  *   instruction stream; 4: every wavefront the matrix role; 5: every wavefront the
- *   vector role; 6: each thread writes its wavefront's SIMD index (placement check).
+ *   vector role; 6: each thread writes its wavefront's SIMD index (placement check);
+ *   8 + m (m = 0..5): mode m, writing instead of checksums each wavefront's elapsed
+ *   shader-clock cycles (lanes 0-31) and 100 MHz real-time ticks (lanes 32-63).
  *   Each role runs exactly `iters` rounds.
  *   out : [blocks * 512] float32, written: each thread's checksum (mode 6: SIMD index;
- *         0 for a wavefront with no role).
- *   1 <= blocks <= 2^20, iters >= 0 (FA_ERR_SHAPE); mode in 0..6 (FA_ERR_ARG).
+ *         modes 8-13: elapsed cycles or ticks; 0 for a wavefront with no role).
+ *   1 <= blocks <= 2^20, iters >= 0 (FA_ERR_SHAPE); mode in 0..6 or 8..13 (FA_ERR_ARG).
  */
 int fa_calibrate_overlap(float* out, int blocks, int iters, int mode, void* stream);
 int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks, void* stream);

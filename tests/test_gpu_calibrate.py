@@ -104,5 +104,18 @@ def test_overlap_probe_placement_and_checksums():
 
 def test_overlap_probe_rejects_bad_mode():
     out = torch.empty(512, device="cuda")
-    with pytest.raises(fa.FaError):
-        fa.fa_calibrate_overlap(out, 1, 1, 7)
+    for mode in (7, 14, -1):
+        with pytest.raises(fa.FaError):
+            fa.fa_calibrate_overlap(out, 1, 1, mode)
+
+
+def test_overlap_probe_timed_modes_report_cycles_and_ticks():
+    blocks = 8
+    out = torch.full((blocks * 512,), float("nan"), device="cuda")
+    fa.fa_calibrate_overlap(out, blocks, 64, 8 + 2)
+    torch.cuda.synchronize()
+    t = out.view(blocks, 8, 64).cpu()
+    cyc, ticks = t[:, :, :32], t[:, :, 32:]
+    assert torch.all(cyc > 0) and torch.all(ticks > 0)
+    mhz = (cyc[:, :, 0] / ticks[:, :, 0]).median() * 100
+    assert 500 < float(mhz) < 3500, float(mhz)
