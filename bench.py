@@ -227,6 +227,9 @@ def bench_decode(steps: int, warmup: int, torch, fa, make_inputs, W):
     ms_step = time_launches(step, steps, warmup, torch)
     ms_part = time_launches(partials, steps, warmup, torch)
     ms_comb = time_launches(combine, steps, warmup, torch)
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    ms_noalloc = time_launches(lambda: fa.fa_decode_noalloc(qd, kd, vd, o2, lse2, w.scale, S),
+                               steps, warmup, torch)
     esz = 2
     kv_bytes = 2 * w.B * w.H * w.L * w.D * esz
     q_bytes = w.B * w.H * w.D * esz
@@ -238,6 +241,7 @@ def bench_decode(steps: int, warmup: int, torch, fa, make_inputs, W):
     res = {
         "workload": DECODE, "value": step_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
         "ms_per_step": ms_step, "ms_partials": ms_part, "ms_combine": ms_comb,
+        "ms_noalloc": ms_noalloc, "noalloc_gbs": step_bytes / (ms_noalloc * 1e-3) / 1e9,
         "bytes_per_step": step_bytes,
         "config": {"B": w.B, "H": w.H, "L": w.L, "D": w.D, "splits": S, "dtype": "bf16"},
         "roofline": {"kernel": "decode_partials_kernel", "bound": "hbm", "achieved": achieved,
@@ -245,7 +249,7 @@ def bench_decode(steps: int, warmup: int, torch, fa, make_inputs, W):
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes,
                      "read_bytes": part_bytes, "write_bytes": BH * S * (D + 2) * 4},
     }
-    del qd, kd, vd
+    del qd, kd, vd, o2, lse2
     torch.cuda.empty_cache()
     res["one_gpu_share"] = bench_decode_share(steps, warmup, torch, fa, q, k, v, w)
     return res

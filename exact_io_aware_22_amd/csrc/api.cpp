@@ -42,6 +42,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, m/d/lse/delta 4-byte alignment)";
     case FA_ERR_ARG: return "invalid argument: scale must be finite and > 0, causal 0 or 1, windows >= -1";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    case FA_ERR_SCRATCH: return "fa_decode_noalloc: the partial states exceed the library's static scratch (2*ceil64(B*H*splits) + B*H*splits*D > FA_DECODE_SCRATCH_FLOATS floats)";
     default: return "unknown fa error code";
   }
 }
@@ -100,6 +101,27 @@ int fa_decode_partials(const void* q, const void* k, const void* v, float* m, fl
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(dtype == FA_BF16 ? fa::launch_decode_partials_bf16(a, s)
                                      : fa::launch_decode_partials_f32(a, s));
+}
+
+int fa_decode_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                      int B, int H, int L, int D, float scale, int splits, int dtype,
+                      void* stream) {
+  static_assert(fa::kDecodeScratchFloats == FA_DECODE_SCRATCH_FLOATS, "one capacity");
+  if (B < 0 || H < 0 || L < 0 || splits < 1 || !head_dim_ok(D) || !count_ok(B, H, L, D) ||
+      !count_ok(B, H, splits, D + 2))
+    return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_ARG;
+  if (fa::decode_noalloc_floats(int64_t(B) * H * splits, D) > fa::kDecodeScratchFloats)
+    return FA_ERR_SCRATCH;
+  if (B == 0 || H == 0) return FA_OK;  // empty: no pointer is touched
+  if (!q || !o || !lse || (L > 0 && (!k || !v))) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  fa::DecodeArgs a{q, k, v, nullptr, nullptr, nullptr, B, H, L, D, scale, splits};
+  return hip_status(fa::launch_decode_noalloc(a, dtype == FA_BF16, o, lse,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,

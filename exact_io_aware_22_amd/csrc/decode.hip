@@ -11,6 +11,8 @@
 // 16*R keys per step with non-temporal 16-byte loads that tile whole key rows (R rows
 // per wave-wide load), K and V requests issued together, dot products finished with
 // cross-lane adds inside a row, and the four wavefronts' states merged in LDS.
+#include <mutex>
+
 #include "device.h"
 #include "launch.h"
 
@@ -195,7 +197,58 @@ __global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ M,
   if (t == 0) LSE[r] = den > 0.f ? mx + logf(den) : kNegInf;
 }
 
+// Static scratch of the allocation-free decode: the partial states (m, d, then o_part)
+// of one call. Each GPU the library runs on holds its own copy at its own address. In
+// host code `scratch` only names the symbol: kernels get the device address looked up
+// below, never the array's name.
+__device__ __align__(256) float scratch[kDecodeScratchFloats];
+
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch`, looked up on the first call on that
+// device (with it current) and kept for later calls.
+hipError_t scratch_address(float** out) {
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
+
+int64_t decode_noalloc_floats(int64_t units, int D) {
+  const int64_t padded = (units + 63) / 64 * 64;  // keeps o_part 256-byte aligned
+  return 2 * padded + units * D;
+}
+
+hipError_t launch_decode_noalloc(const DecodeArgs& a, bool bf16, float* o, float* lse,
+                                 hipStream_t s) {
+  float* base = nullptr;
+  hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return e;
+  const int64_t rows = int64_t(a.B) * a.H;
+  const int64_t padded = (rows * a.splits + 63) / 64 * 64;
+  DecodeArgs p = a;
+  p.m = base;
+  p.d = base + padded;
+  p.o_part = base + 2 * padded;
+  e = bf16 ? launch_decode_partials_bf16(p, s) : launch_decode_partials_f32(p, s);
+  if (e != hipSuccess) return e;
+  const CombineArgs c{p.m, p.d, p.o_part, o, lse, int(rows), a.splits, a.D};
+  return launch_combine_partials(c, s);
+}
 
 hipError_t launch_decode_partials_bf16(const DecodeArgs& a, hipStream_t s) {
   return a.D == 128 ? launch_partials<true, 128>(a, s) : launch_partials<true, 64>(a, s);

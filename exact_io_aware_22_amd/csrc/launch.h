@@ -72,6 +72,13 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_decode_partials_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_partials_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine_partials(const CombineArgs& a, hipStream_t s);
+// Partials into the library's static scratch, then their merge into o, lse.
+hipError_t launch_decode_noalloc(const DecodeArgs& a, bool bf16, float* o, float* lse,
+                                 hipStream_t s);
+// Floats of static scratch the decode of B*H*splits units at head dim D needs (m and d
+// padded to 64 floats each, then o_part), and the capacity.
+int64_t decode_noalloc_floats(int64_t units, int D);
+constexpr int64_t kDecodeScratchFloats = int64_t(1) << 23;
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_softmax_stats(const RowReduceArgs& a, hipStream_t s);

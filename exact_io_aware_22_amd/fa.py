@@ -24,7 +24,7 @@ _lib = None
 FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
-            "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
+            "fa_decode_noalloc", "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
             "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
             "fa_abi_version")
 
@@ -57,6 +57,8 @@ def load():
         getattr(lib, name).restype = i
     lib.fa_decode_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_decode_partials.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_decode_noalloc.restype = i
     lib.fa_combine_partials.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
     lib.fa_combine_partials.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
@@ -219,6 +221,27 @@ def fa_decode_partials(q, k, v, m, d, o_part, scale: float, splits: int, stream=
     code = load().fa_decode_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(d), _ptr(o_part),
                                      B, H, L, D, float(scale), splits, dt, _stream(stream))
     _check(code, "fa_decode_partials")
+
+
+def fa_decode_noalloc(q, k, v, o, lse, scale: float, splits: int, stream=None) -> None:
+    """Partials and merge in one call, the partial states in the library's static
+    scratch (no allocation). q: [B, H, 1, D] or [B, H, D]; k, v: [B, H, L, D];
+    o: [B*H, D] fp32; lse: [B*H] fp32. Calls that overlap on one GPU race on that
+    scratch; calls on one stream are ordered."""
+    if k.dim() != 4:
+        raise ValueError(f"k must be [B, H, L, D], got shape {tuple(k.shape)}")
+    B, H, L, D = k.shape
+    splits = int(splits)
+    if splits < 1:
+        raise ValueError("splits must be >= 1")
+    if tuple(q.shape) not in ((B, H, 1, D), (B, H, D)):
+        raise ValueError(f"q must have shape {(B, H, 1, D)} or {(B, H, D)}, got {tuple(q.shape)}")
+    dt = _same_input_dtype(k=k, q=q, v=v)
+    _checked({"v": k.shape, "o": (B * H, D), "lse": (B * H,)}, ("o", "lse"),
+             q=q, k=k, v=v, o=o, lse=lse)
+    code = load().fa_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, L, D,
+                                    float(scale), splits, dt, _stream(stream))
+    _check(code, "fa_decode_noalloc")
 
 
 def fa_combine_partials(m, d, o_part, o, lse, stream=None) -> None:

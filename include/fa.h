@@ -53,10 +53,16 @@ enum {
                         not 4-byte aligned; a row-reduction input not aligned to its
                         element                                                     */
   FA_ERR_HIP = -5,   /* the HIP runtime rejected the kernel launch                   */
-  FA_ERR_ARG = -6    /* scale not finite or not > 0, causal not 0 or 1, or a window
+  FA_ERR_ARG = -6,   /* scale not finite or not > 0, causal not 0 or 1, or a window
                         bound below -1 (numbered after FA_ERR_HIP so the first five
                         codes keep the values of the original five-code interface) */
+  FA_ERR_SCRATCH = -7 /* fa_decode_noalloc: the partial states need more than the
+                         library's static scratch (FA_DECODE_SCRATCH_FLOATS)         */
 };
+
+/* Capacity, in floats, of the static device array fa_decode_noalloc keeps its
+   partial states in (32 MiB per GPU). */
+#define FA_DECODE_SCRATCH_FLOATS 8388608
 
 /*
  * fa_forward -- exact attention forward with log-sum-exp.
@@ -127,6 +133,32 @@ int fa_forward_ext(const void* q, const void* k, const void* v, float* o, float*
 int fa_decode_partials(const void* q, const void* k, const void* v, float* m, float* d,
                        float* o_part, int B, int H, int L, int D, float scale, int splits,
                        int dtype, void* stream);
+
+/*
+ * fa_decode_noalloc -- fa_decode_partials followed by fa_combine_partials in one call
+ * that allocates nothing: the partial states live in a static device array of the
+ * library instead of caller scratch. For callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same kernels, so the same results as the two calls with caller scratch.
+ *
+ *   q, k, v, B, H, L, D, scale, splits, dtype : as for fa_decode_partials.
+ *   o       : [B*H][D] float32, written: the merged o / d of every head.
+ *   lse     : [B*H] float32, written: the merged log-sum-exp (-inf for L = 0).
+ *   Limit: with R = B*H*splits and R64 = R rounded up to a multiple of 64,
+ *   2*R64 + R*D <= FA_DECODE_SCRATCH_FLOATS (m and d, then o_part, 256-byte aligned);
+ *   a larger problem returns FA_ERR_SCRATCH before anything is launched. The
+ *   split-KV decode of 16 x 32 heads at D = 128 in 64 chunks uses 4.26 M of the 8.39 M.
+ *   Sharing: each GPU holds one such array (32 MiB, kept until the process ends), and
+ *   every call on that GPU uses it. Calls that overlap on one GPU (other streams, other
+ *   host threads) race on it and must be ordered by the caller; calls on one stream
+ *   are ordered by the stream. Nothing in it needs clearing: every call writes all the
+ *   states it reads.
+ *   The first call on a device looks up that device's address of the array (a host
+ *   query, no allocation); later calls reuse it.
+ */
+int fa_decode_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                      int B, int H, int L, int D, float scale, int splits, int dtype,
+                      void* stream);
 
 /*
  * fa_combine_partials -- fold partial states with the combine of section "The

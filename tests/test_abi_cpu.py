@@ -16,7 +16,7 @@ from exact_io_aware_22_amd import fa
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "fa.h"
 
-OK, NULL, SHAPE, DTYPE, ALIGN, HIP, ARG = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, DTYPE, ALIGN, HIP, ARG, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 P = 1 << 20  # a fake, 16-byte-aligned, never dereferenced address
 
 
@@ -36,6 +36,7 @@ def lib():
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
+         "fa_decode_noalloc",
          "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
          "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
          "fa_abi_version"])
@@ -53,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_strerror(lib):
     assert lib.fa_abi_version() == 1
-    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, HIP, ARG, 12345):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, HIP, ARG, SCRATCH, 12345):
         msg = fa.strerror(code)
         assert isinstance(msg, str) and msg
 
@@ -231,3 +232,49 @@ def test_calibration_validation(lib):
     assert wr(P + 8, 1024, 1, 4, None) == ALIGN
 
 
+
+SCRATCH_FLOATS = 8388608
+
+
+def dec_noalloc(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=2, L=64, D=128, scale=0.1, splits=4,
+                dtype=1):
+    return lib.fa_decode_noalloc(q, k, v, o, lse, B, H, L, D, scale, splits, dtype, None)
+
+
+def test_decode_noalloc_validation(lib):
+    header = HEADER.read_text()
+    assert f"#define FA_DECODE_SCRATCH_FLOATS {SCRATCH_FLOATS}" in header
+    assert dec_noalloc(lib, splits=0) == SHAPE
+    assert dec_noalloc(lib, D=96) == SHAPE
+    assert dec_noalloc(lib, L=-1) == SHAPE
+    assert dec_noalloc(lib, dtype=3) == DTYPE
+    assert dec_noalloc(lib, scale=0.0) == ARG
+    assert dec_noalloc(lib, q=None) == NULL
+    assert dec_noalloc(lib, lse=None) == NULL
+    assert dec_noalloc(lib, o=P + 4) == ALIGN
+    assert dec_noalloc(lib, B=0) == OK and dec_noalloc(lib, H=0, q=None) == OK
+    # the limit: 2 * ceil64(R) + R * D floats, R = B * H * splits
+    def need(R, D):
+        return 2 * (-(-R // 64) * 64) + R * D
+    assert need(16 * 32 * 64, 128) <= SCRATCH_FLOATS  # the split-KV decode workload fits
+    R_max = max(R for R in range(SCRATCH_FLOATS // 130 - 64, SCRATCH_FLOATS // 130 + 64)
+                if need(R, 128) <= SCRATCH_FLOATS)
+    # R_max units fit; one more does not; checked before any launch, whatever L is
+    assert dec_noalloc(lib, B=1, H=1, splits=R_max + 1, L=1 << 20) == SCRATCH
+    assert dec_noalloc(lib, B=R_max + 1, H=1, splits=1) == SCRATCH
+    assert dec_noalloc(lib, B=16, H=32, splits=1024) == SCRATCH
+    assert dec_noalloc(lib, B=16, H=32, splits=1024, D=64, L=0, k=None, v=None) == SCRATCH
+    assert dec_noalloc(lib, B=1, H=1, splits=R_max + 1, D=64, q=None) == NULL  # fits at D=64
+    assert "static scratch" in fa.strerror(SCRATCH)
+
+
+def test_library_imports_no_allocator():
+    """Nothing in libfa.so allocates device or host memory: no HIP allocation routine
+    is even imported (the static scratch of fa_decode_noalloc is a device global)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", str(fa._LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    imported = set(re.findall(r"\bU\s+(\S+?)(?:@\S+)?$", out, flags=re.M))
+    allocators = {n for n in imported if re.match(r"hip(Ext)?(Host|Managed)?(Malloc|Free|Alloc)", n)
+                  or n.startswith("hipMemPool") or n.startswith("hipMallocAsync")}
+    assert not allocators, allocators
+    assert "hipGetSymbolAddress" in imported
