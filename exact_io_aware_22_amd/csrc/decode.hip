@@ -157,13 +157,121 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partials_kernel(
   }
 }
 
+// Chunks of at most one wavefront step of keys (KW): every wavefront folds whole
+// (head, chunk) units by itself, kWaveUnits in turn, and writes each unit's state
+// straight from registers. With the four wavefronts of the kernel above sharing such a
+// unit, three would have no keys; here none idles and no LDS merge is needed.
+constexpr int kWaveUnits = 2;
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(64 * kWaves) void decode_partials_wave_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    float* __restrict__ Mo, float* __restrict__ Do, float* __restrict__ Op, int L, int splits,
+    int64_t units, int chunk, float c, float scale) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int E = 16 / ESZ;       // elements per 16-byte load
+  constexpr int LPR = D / E;        // lanes per key row
+  constexpr int RPW = 64 / LPR;     // key rows per wave-wide load
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane / LPR, col = (lane % LPR) * E;
+  const int64_t rowbytes = int64_t(D) * ESZ;
+  for (int t = 0; t < kWaveUnits; ++t) {
+    const int64_t unit = (int64_t(blockIdx.x) * kWaves + wave) * kWaveUnits + t;
+    if (unit >= units) break;  // uniform within the wavefront
+    const int split = int(unit % splits);
+    const int64_t bh = unit / splits;
+    const int64_t j0l = int64_t(split) * chunk;
+    const int j0 = int(j0l < L ? j0l : L);
+    const int j1 = int(j0l + chunk < L ? j0l + chunk : L);  // j1 - j0 <= kLoads * RPW
+    const uint8_t* Kh = K + bh * L * rowbytes + col * ESZ;
+    const uint8_t* Vh = V + bh * L * rowbytes + col * ESZ;
+    const u32x4_t qw = load16(Q + bh * rowbytes + col * ESZ);
+    u32x4_t kr[kLoads], vr[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int key = j0 + i * RPW + row;
+      const bool ok = key < j1;
+      kr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kh + int64_t(key) * rowbytes))
+                 : u32x4_t{0, 0, 0, 0};
+      vr[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vh + int64_t(key) * rowbytes))
+                 : u32x4_t{0, 0, 0, 0};
+    }
+    float s[kLoads];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      float p = 0.f;
+      if constexpr (BF16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          p = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[i][w]), as_bf16x2(qw[w]), p, false);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) p = fmaf(__uint_as_float(kr[i][w]), __uint_as_float(qw[w]), p);
+      }
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) p += __shfl_xor(p, off);
+      s[i] = (j0 + i * RPW + row < j1) ? p : kNegInf;
+      mx = fmaxf(mx, s[i]);
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float nmc = -(mx == kNegInf ? 0.f : mx) * c;
+    float den = 0.f;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const float p = exp2_hw(fmaf(s[i], c, nmc));
+      den += p;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (BF16) {
+          o[2 * w] = fmaf(p, bf16_lo(vr[i][w]), o[2 * w]);
+          o[2 * w + 1] = fmaf(p, bf16_hi(vr[i][w]), o[2 * w + 1]);
+        } else {
+          o[w] = fmaf(p, __uint_as_float(vr[i][w]), o[w]);
+        }
+      }
+    }
+    // Sum the key rows of the wavefront (one reference maximum for all of them).
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      den += __shfl_xor(den, off);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] += __shfl_xor(o[e], off);
+    }
+    const int64_t out = bh * splits + split;
+    if (lane < LPR) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) Op[out * D + col + e] = o[e];
+    }
+    if (lane == 0) {
+      Mo[out] = mx == kNegInf ? kNegInf : mx * scale;
+      Do[out] = den;
+    }
+  }
+}
+
 template <bool BF16, int D>
 hipError_t launch_partials(const DecodeArgs& a, hipStream_t s) {
   const int64_t BH = int64_t(a.B) * a.H;
   const int64_t units = BH * a.splits;
+  const int chunk = int((int64_t(a.L) + a.splits - 1) / a.splits);
+  constexpr int KW = kLoads * (64 / (D / (16 / (BF16 ? 2 : 4))));  // keys per wavefront step
+  if (chunk <= KW) {
+    const int64_t per_block = int64_t(kWaves) * kWaveUnits;
+    const int64_t blocks = (units + per_block - 1) / per_block;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_partials_wave_kernel<BF16, D>), dim3(unsigned(blocks)),
+                       dim3(64 * kWaves), 0, s, static_cast<const uint8_t*>(a.q),
+                       static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.m,
+                       a.d, a.o_part, a.L, a.splits, units, chunk, a.scale * kLog2e, a.scale);
+    return hipGetLastError();
+  }
   const int64_t blocks = (units + kUnits - 1) / kUnits;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const int chunk = int((int64_t(a.L) + a.splits - 1) / a.splits);
   hipLaunchKernelGGL((decode_partials_kernel<BF16, D>), dim3(unsigned(blocks)), dim3(64 * kWaves),
                      0, s, static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
                      static_cast<const uint8_t*>(a.v), a.m, a.d, a.o_part, a.L, a.splits, units,
@@ -171,30 +279,78 @@ hipError_t launch_partials(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// One workgroup of 256 threads per row: thread t owns head dim t mod D of group t / D;
+// the groups split the partials between them. First the row's maximum (every thread
+// strides over the partials' m, then a workgroup reduction), then each group folds its
+// partials with weights e^{m_s - M}, four partials in flight per thread, and the
+// groups' sums are added in LDS. Identity partials (m = -inf) contribute nothing.
+constexpr int kCombineThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(const float* __restrict__ M,
-                                                    const float* __restrict__ Dn,
-                                                    const float* __restrict__ Op,
-                                                    float* __restrict__ O,
-                                                    float* __restrict__ LSE, int splits) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ M,
+                                                                 const float* __restrict__ Dn,
+                                                                 const float* __restrict__ Op,
+                                                                 float* __restrict__ O,
+                                                                 float* __restrict__ LSE,
+                                                                 int splits) {
+  constexpr int G = kCombineThreads / D;  // groups of partials
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ float acc_s[G][D], den_s[G];
   const int64_t r = blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int dd = t % D, g = t / D;
   const float* mr = M + r * splits;
   const float* dr = Dn + r * splits;
-  const float* orow = Op + r * splits * D + t;
+  const float* orow = Op + r * splits * D + dd;
+
   float mx = kNegInf;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, mr[s]);
+  for (int s = t; s < splits; s += kCombineThreads) mx = fmaxf(mx, mr[s]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) mx = fmaxf(mx, red[w]);
   const float mref = mx == kNegInf ? 0.f : mx;
+
   float den = 0.f, acc = 0.f;
-  for (int s = 0; s < splits; ++s) {
+  int s = g;
+  for (; s + 3 * G < splits; s += 4 * G) {
+    float ms[4], ds[4], os[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ms[u] = mr[s + u * G];
+      ds[u] = dr[s + u * G];
+      os[u] = orow[int64_t(s + u * G) * D];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (ms[u] == kNegInf) continue;  // the identity contributes nothing
+      const float f = exp2_hw((ms[u] - mref) * kLog2e);
+      den = fmaf(f, ds[u], den);
+      acc = fmaf(f, os[u], acc);
+    }
+  }
+  for (; s < splits; s += G) {
     const float ms = mr[s];
-    if (ms == kNegInf) continue;  // the identity contributes nothing
+    if (ms == kNegInf) continue;
     const float f = exp2_hw((ms - mref) * kLog2e);
     den = fmaf(f, dr[s], den);
     acc = fmaf(f, orow[int64_t(s) * D], acc);
   }
-  O[r * D + t] = den > 0.f ? acc / den : 0.f;
-  if (t == 0) LSE[r] = den > 0.f ? mx + logf(den) : kNegInf;
+  acc_s[g][dd] = acc;
+  if (dd == 0) den_s[g] = den;
+  __syncthreads();
+  if (g == 0) {
+    float a = acc, dn = den;
+#pragma unroll
+    for (int h = 1; h < G; ++h) {
+      a += acc_s[h][dd];
+      dn += den_s[h];
+    }
+    O[r * D + dd] = dn > 0.f ? a / dn : 0.f;
+    if (dd == 0) LSE[r] = dn > 0.f ? mx + logf(dn) : kNegInf;
+  }
 }
 
 // Static scratch of the allocation-free decode: the partial states (m, d, then o_part)
@@ -260,11 +416,11 @@ hipError_t launch_decode_partials_f32(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_combine_partials(const CombineArgs& a, hipStream_t s) {
   if (a.D == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(unsigned(a.rows)), dim3(128), 0, s, a.m, a.d,
-                       a.o_part, a.o, a.lse, a.splits);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(unsigned(a.rows)), dim3(kCombineThreads), 0,
+                       s, a.m, a.d, a.o_part, a.o, a.lse, a.splits);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(unsigned(a.rows)), dim3(64), 0, s, a.m, a.d,
-                       a.o_part, a.o, a.lse, a.splits);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(unsigned(a.rows)), dim3(kCombineThreads), 0, s,
+                       a.m, a.d, a.o_part, a.o, a.lse, a.splits);
   return hipGetLastError();
 }
 
