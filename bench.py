@@ -136,7 +136,9 @@ def time_each(fn, calls: int, torch):
 def measured_ceilings(steps: int, warmup: int, torch, fa):
     """The chip's sustained rates, the denominators of the fractions of measured (not
     published) peaks: the library's MFMA-only loop (random bf16 register operands, two
-    wavefronts per SIMD) and its read-only stream (16-byte non-temporal loads of 2 GiB).
+    wavefronts per SIMD), its read-only and write-only streams (16-byte non-temporal loads
+    and stores of 2 GiB), and its copy from one read into two write streams at the prefix
+    scans' byte ratios.
     A bf16 GEMM (torch.mm) and a device copy are reported beside them as library
     references."""
     blocks, iters = 1024, 256
@@ -156,7 +158,20 @@ def measured_ceilings(steps: int, warmup: int, torch, fa):
                                       warmup, torch))
         del fold
     ms_read, ms_write = min(ms_read), min(ms_write)
-    del chk
+    del chk, x
+    # one read and two write streams at the prefix scans' byte ratios (each output 1x the
+    # input for float32 input, 2x for bfloat16), no arithmetic: 1 GiB read
+    mbytes = 1 << 30
+    mx = torch.ones(mbytes // 4, dtype=torch.int32, device="cuda")
+    mix = {}
+    for ratio in (1, 2):
+        my = torch.empty(2 * ratio * mbytes // 4, dtype=torch.int32, device="cuda")
+        ms_mix = min(time_launches(lambda: fa.fa_calibrate_mix(mx, my, ratio, mblocks), steps,
+                                   warmup, torch) for mblocks in (8192, 16384, 32768))
+        mix[str(ratio)] = (1 + 2 * ratio) * mbytes / (ms_mix * 1e-3) / 1e9
+        del my
+    del mx
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     n = 8192
     g = torch.Generator(device="cuda").manual_seed(0)
     a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
@@ -178,6 +193,9 @@ def measured_ceilings(steps: int, warmup: int, torch, fa):
         "write_gbs": nbytes / (ms_write * 1e-3) / 1e9,
         "write": f"fa_calibrate_write: {nbytes >> 30} GiB, 16-byte non-temporal stores, best of "
                  "512 and 1024 workgroups",
+        "mix_gbs": mix,
+        "mix": "fa_calibrate_mix: 1 GiB read, written to two streams of ratio x 1 GiB (keys: "
+               "ratio), bytes read + written per second, best of 8192, 16384 and 32768 workgroups",
         "library_reference": {
             "bf16_gemm_tflops": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
             "bf16_gemm": f"torch.mm {n}x{n}x{n}, N(0, 1) operands",
@@ -640,6 +658,11 @@ def main() -> int:
                 r["frac_of_measured"] = stream_fraction(
                     r["read_bytes"], r["write_bytes"], r["algorithmic_bytes_per_launch"],
                     r["achieved"], ceil["read_gbs"], ceil["write_gbs"])
+                # a scan reads one stream and writes two: against a plain copy with the
+                # same mix (reads and writes at once cost more than either stream alone)
+                ratio = str(round(r["write_bytes"] / (2 * r["read_bytes"])))
+                if r.get("kernel", "").startswith("row_scan_kernel") and ratio in ceil["mix_gbs"]:
+                    r["frac_of_same_mix_copy"] = r["achieved"] / ceil["mix_gbs"][ratio]
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)
     return 0

@@ -254,4 +254,16 @@ int fa_calibrate_write(void* y, long long nbytes, unsigned value, int blocks, vo
                                                static_cast<hipStream_t>(stream)));
 }
 
+int fa_calibrate_mix(const void* x, long long nbytes, void* y, int ratio, int blocks,
+                     void* stream) {
+  if (blocks < 1 || blocks > (1 << 22) || nbytes < 0 || nbytes % 4096 != 0 ||
+      (ratio != 1 && ratio != 2 && ratio != 4))
+    return FA_ERR_SHAPE;
+  if (nbytes == 0) return FA_OK;  // empty: no pointer is touched, nothing is launched
+  if (!x || !y) return FA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_calibrate_mix(x, nbytes, y, ratio, blocks,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -11,6 +11,10 @@
 //     be elided.
 //   * write_stream_kernel: the same split with 16-byte non-temporal stores of a
 //     checkable pattern.
+//   * mix_stream_kernel: the same split, read, and every word written to two output
+//     streams `ratio` times over: the traffic of a kernel that reads one stream and
+//     writes two (the prefix scans), with no arithmetic, so its rate is the ceiling for
+//     that mix of reads and writes.
 #include "device.h"
 #include "launch.h"
 
@@ -227,6 +231,39 @@ __global__ __launch_bounds__(kReadThreads) void write_stream_kernel(u32x4_t* __r
     __builtin_nontemporal_store(u32x4_t{value, uint32_t(i), value, uint32_t(i)}, y + i);
 }
 
+// Workgroup b reads its span (the read stream's split, whole runs of 256 words) two
+// runs at a time, and writes the run of 256 words at j to words ratio j + 256 r + t
+// (r < ratio) of both output streams: every store instruction is one contiguous run.
+template <int RATIO>
+__global__ __launch_bounds__(kReadThreads) void mix_stream_kernel(const u32x4_t* __restrict__ x,
+                                                                   int64_t n16, int64_t span,
+                                                                   u32x4_t* __restrict__ y0,
+                                                                   u32x4_t* __restrict__ y1) {
+  const int64_t b0 = int64_t(blockIdx.x) * span;
+  const int64_t end = min(n16, b0 + span);  // a multiple of 256: n16 and span are
+  const int t = threadIdx.x;
+  for (int64_t j = b0; j < end; j += 2 * kReadThreads) {
+    const bool two = j + kReadThreads < end;  // uniform
+    const u32x4_t v0 = __builtin_nontemporal_load(x + j + t);
+    u32x4_t v1 = {};
+    if (two) v1 = __builtin_nontemporal_load(x + j + kReadThreads + t);
+#pragma unroll
+    for (int r = 0; r < RATIO; ++r) {
+      const int64_t o = RATIO * j + kReadThreads * r + t;
+      __builtin_nontemporal_store(v0, y0 + o);
+      __builtin_nontemporal_store(v0, y1 + o);
+    }
+    if (two) {
+#pragma unroll
+      for (int r = 0; r < RATIO; ++r) {
+        const int64_t o = RATIO * (j + kReadThreads) + kReadThreads * r + t;
+        __builtin_nontemporal_store(v1, y0 + o);
+        __builtin_nontemporal_store(v1, y1 + o);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_calibrate_mfma(float* out, int blocks, int iters, uint32_t seed,
@@ -259,6 +296,27 @@ hipError_t launch_calibrate_write(void* y, int64_t nbytes, uint32_t value, int b
   const int64_t span = ((n16 + blocks - 1) / blocks + kReadThreads - 1) / kReadThreads * kReadThreads;
   hipLaunchKernelGGL(write_stream_kernel, dim3(unsigned(blocks)), dim3(kReadThreads), 0, s,
                      static_cast<u32x4_t*>(y), n16, span, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate_mix(const void* x, int64_t nbytes, void* y, int ratio, int blocks,
+                                hipStream_t s) {
+  const int64_t n16 = nbytes / 16;
+  const int64_t span = ((n16 + blocks - 1) / blocks + kReadThreads - 1) / kReadThreads * kReadThreads;
+  const u32x4_t* in = static_cast<const u32x4_t*>(x);
+  u32x4_t* y0 = static_cast<u32x4_t*>(y);
+  u32x4_t* y1 = y0 + ratio * n16;
+  if (ratio == 1)
+    hipLaunchKernelGGL(mix_stream_kernel<1>, dim3(unsigned(blocks)), dim3(kReadThreads), 0, s, in,
+                       n16, span, y0, y1);
+  else if (ratio == 2)
+    hipLaunchKernelGGL(mix_stream_kernel<2>, dim3(unsigned(blocks)), dim3(kReadThreads), 0, s, in,
+                       n16, span, y0, y1);
+  else if (ratio == 4)
+    hipLaunchKernelGGL(mix_stream_kernel<4>, dim3(unsigned(blocks)), dim3(kReadThreads), 0, s, in,
+                       n16, span, y0, y1);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

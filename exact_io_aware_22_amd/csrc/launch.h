@@ -94,5 +94,7 @@ hipError_t launch_calibrate_read(const void* x, int64_t nbytes, uint32_t* out, i
                                  hipStream_t s);
 hipError_t launch_calibrate_write(void* y, int64_t nbytes, uint32_t value, int blocks,
                                   hipStream_t s);
+hipError_t launch_calibrate_mix(const void* x, int64_t nbytes, void* y, int ratio, int blocks,
+                                hipStream_t s);
 
 }  // namespace fa

@@ -36,6 +36,21 @@ namespace {
 
 constexpr int kK = 8;  // elements per block
 
+// v moved between lanes by the data-parallel primitive CTRL, written only in the rows of
+// 16 lanes that ROWS selects; a lane that is not written, or whose source lies outside
+// its row, gets `fill`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp(float fill, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROWS, 0xf, false));
+}
+
+// Lane l's value of v, for every lane (a scalar register read).
+__device__ __forceinline__ float readlane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 // ---------------------------------------------------------------- the two monoids
 struct SoftmaxMonoid {
   struct S {
@@ -44,22 +59,30 @@ struct SoftmaxMonoid {
   __device__ static S identity() { return {kNegInf, 0.f}; }
   __device__ static S inject(float x) { return x == kNegInf ? identity() : S{x, 1.f}; }
   // Both sides rescaled to the larger maximum: the side that holds it keeps its d, the
-  // other is scaled by e^{(its m) - m}, one exponential per combine. A side at -inf
-  // contributes 2^-inf = 0; when both are -inf the factor is 0 and no -inf - (-inf)
-  // arises.
+  // other is scaled by e^{-|b.m - a.m|}, one exponential per combine. A side at -inf
+  // contributes 2^-inf = 0; when both are -inf the difference is NaN, which the maximum
+  // with -inf (it returns the number) turns into -inf, so d = 0 + 0 stays exact. The
+  // maximum of the two m is IEEE 754-2019's, which takes its operands as they are (no
+  // quieting step).
   __device__ static S combine(S a, S b) {
-    const float m = fmaxf(a.m, b.m), lo = fminf(a.m, b.m);
-    const float e = m == kNegInf ? 0.f : exp2_hw((lo - m) * kLog2e);
-    return {m, a.m >= b.m ? fmaf(b.d, e, a.d) : fmaf(a.d, e, b.d)};
+    const float t = fmaxf((b.m - a.m) * kLog2e, kNegInf);
+    const float e = exp2_hw(-fabsf(t));
+    return {__builtin_elementwise_maximum(a.m, b.m), t <= 0.f ? fmaf(b.d, e, a.d) : fmaf(a.d, e, b.d)};
+  }
+  // combine(s, inject(x)), with the injected d = 1 folded in.
+  __device__ static S push(S s, float x) {
+    const float t = fmaxf((x - s.m) * kLog2e, kNegInf);
+    const float e = exp2_hw(-fabsf(t));
+    return {__builtin_elementwise_maximum(s.m, x), t <= 0.f ? s.d + e : fmaf(s.d, e, 1.f)};
   }
   // Merge the fold of K injections into s: the running maximum takes the block's
   // maximum, d is rescaled once to it, then the block's shifted exponentials add.
   template <int K>
   __device__ static S absorb(S s, const float (&x)[K]) {
-    float mx = fmaxf(x[0], x[1]);
+    float mx = __builtin_elementwise_maximum(x[0], x[1]);
 #pragma unroll
-    for (int i = 2; i < K; ++i) mx = fmaxf(mx, x[i]);
-    const float m = fmaxf(s.m, mx);
+    for (int i = 2; i < K; ++i) mx = __builtin_elementwise_maximum(mx, x[i]);
+    const float m = __builtin_elementwise_maximum(s.m, mx);
     const float mr = m == kNegInf ? 0.f : m;
     float d = s.d * exp2_hw((s.m - mr) * kLog2e);
 #pragma unroll
@@ -71,6 +94,24 @@ struct SoftmaxMonoid {
   }
   __device__ static S shfl_up(S s, int delta) {
     return {__shfl_up(s.m, delta), __shfl_up(s.d, delta)};
+  }
+  __device__ static S readlane(S s, int l) { return {fa::readlane(s.m, l), fa::readlane(s.d, l)}; }
+  template <int CTRL, int ROWS>
+  __device__ static S dpp(S s) {
+    return {fa::dpp<CTRL, ROWS>(kNegInf, s.m), fa::dpp<CTRL, ROWS>(0.f, s.d)};
+  }
+  // The fold of K injections: their maximum, and the sum of each one's exponential
+  // relative to it.
+  template <int K>
+  __device__ static S of_block(const float (&x)[K]) {
+    float m = __builtin_elementwise_maximum(x[0], x[1]);
+#pragma unroll
+    for (int i = 2; i < K; ++i) m = __builtin_elementwise_maximum(m, x[i]);
+    const float mr = m == kNegInf ? 0.f : m;
+    float d = exp2_hw((x[0] - mr) * kLog2e);
+#pragma unroll
+    for (int i = 1; i < K; ++i) d += exp2_hw((x[i] - mr) * kLog2e);
+    return {m, d};
   }
   __device__ static void store(S s, float* out0, float* out1, int64_t row) {
     out0[row] = s.m;
@@ -94,6 +135,12 @@ struct WelfordMonoid {
     const float delta = b.mu - a.mu, r = b.n * __builtin_amdgcn_rcpf(n);
     return {n, a.mu + delta * r, a.m2 + b.m2 + delta * delta * a.n * r};
   }
+  // combine(s, inject(x)): Welford's one-sample update.
+  __device__ static S push(S s, float x) {
+    const float n = s.n + 1.f, delta = x - s.mu;
+    const float mu = fmaf(delta, __builtin_amdgcn_rcpf(n), s.mu);
+    return {n, mu, fmaf(delta, x - mu, s.m2)};
+  }
   // The block's own triple (K, mean, squared deviations from it), merged into s.
   template <int K>
   __device__ static S absorb(S s, const float (&x)[K]) {
@@ -114,6 +161,29 @@ struct WelfordMonoid {
   }
   __device__ static S shfl_up(S s, int delta) {
     return {__shfl_up(s.n, delta), __shfl_up(s.mu, delta), __shfl_up(s.m2, delta)};
+  }
+  __device__ static S readlane(S s, int l) {
+    return {fa::readlane(s.n, l), fa::readlane(s.mu, l), fa::readlane(s.m2, l)};
+  }
+  template <int CTRL, int ROWS>
+  __device__ static S dpp(S s) {
+    return {fa::dpp<CTRL, ROWS>(0.f, s.n), fa::dpp<CTRL, ROWS>(0.f, s.mu),
+            fa::dpp<CTRL, ROWS>(0.f, s.m2)};
+  }
+  // The fold of K injections: (K, their mean, their squared deviations from it).
+  template <int K>
+  __device__ static S of_block(const float (&x)[K]) {
+    float sum = x[0] + x[1];
+#pragma unroll
+    for (int i = 2; i < K; ++i) sum += x[i];
+    const float mu = sum * (1.f / K);
+    float m2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const float e = x[i] - mu;
+      m2 = fmaf(e, e, m2);
+    }
+    return {float(K), mu, m2};
   }
   __device__ static void store(S s, float* out0, float* out1, int64_t row) {
     out0[row] = s.mu;
@@ -242,110 +312,193 @@ __global__ __launch_bounds__(256) void row_reduce_kernel(const T* __restrict__ x
 // ---------------------------------------------------------------- the prefix scan
 // Inclusive scan of every row: output j is the state of elements 0..j. A prefix scan is
 // one more re-bracketing any monoid allows (section "Wrap-Up", first point), here on
-// the same pieces: one 256-thread workgroup per row, the row in blocks of 256 x 8
-// elements. Thread t folds its 8 consecutive elements left to right (keeping each
-// partial state), the 256 thread totals are scanned (an inclusive scan across each
-// wavefront with shfl_up, then the four wavefront totals through LDS), and element i
-// of thread t is written as carry + (totals of threads before t) + (its own partial i);
-// the block's total joins the carry for the next block. ALIGNED: x and both outputs
-// start on 16-byte boundaries and rows are whole 16-byte multiples, so a thread's 8
-// elements are read and written with vector accesses.
+// the same pieces: one 256-thread workgroup per row, the row in blocks of 2048
+// elements, wavefront w of a block over elements 512 w .. 512 w + 511 and its lane l
+// over the 8 consecutive elements 8 l .. 8 l + 7. A lane folds its 8 elements into one
+// state; the 64 states are scanned across the wavefront and the four wavefront totals
+// combined through LDS; then the lane folds its elements again, one at a time, onto
+// everything before them (the carry from earlier blocks, earlier wavefronts, earlier
+// lanes) and writes each position's state. The block's total joins the carry.
+//
+// Global memory moves in whole contiguous runs: every load and store instruction of a
+// wavefront covers 1 KB of consecutive bytes (lane l takes 16-byte vector l + 64 j of
+// its wavefront's span), and a per-wavefront LDS area turns those runs into each lane's 8 consecutive elements and
+// back (in for the input, out for each of the two outputs in turn). Vector v of an area
+// sits in slot v ^ ((v >> 3) & 3): eight consecutive lanes that reach for their own
+// vectors (vector P l + k, P = 1 or 2 vectors per lane) then hit eight distinct 16-byte
+// bank groups, as do eight lanes that reach for consecutive vectors.
+//
+// ALIGNED: x and both outputs start on 16-byte boundaries and n is a multiple of the
+// elements in one 16-byte input vector, so every vector is wholly inside the row or
+// wholly past its end. Otherwise each lane reads and writes its elements one by one.
+//
+// Per element a lane spends about 25 vector instructions (the fold, the refold, its
+// share of the scan and of the block's bookkeeping), which keeps the vector ALU well
+// below the time the memory traffic takes.
+constexpr int kOwn = 8;                     // consecutive elements per lane per block
+constexpr int kWaveSpan = 64 * kOwn;        // elements per wavefront per block
+constexpr int kScanBlock = 4 * kWaveSpan;   // elements per workgroup block
+constexpr int kStageVecs = kWaveSpan / 4;   // 16-byte slots per wavefront: one output
+
+// Slot of vector v in a wavefront's LDS area.
+__device__ __forceinline__ int slot(int v) { return v ^ ((v >> 3) & 3); }
+
+// Orders one wavefront's LDS accesses on either side (its lanes exchange data through
+// its own area; no other wavefront touches it).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Inclusive scan across the wavefront: lane l ends with the combine of lanes 0..l, in
+// lane order. Data-parallel primitives move the states: shifts by 1, 2, 4 and 8 within
+// each row of 16 lanes, then the last lane of row 0 (of row 2) into row 1 (row 3), then
+// lane 31 into rows 2 and 3. A lane with no source takes the identity, which combines
+// exactly (the identity is neutral in float32 arithmetic too).
+template <class M>
+__device__ __forceinline__ typename M::S wave_inclusive_scan(typename M::S t) {
+  t = M::combine(M::template dpp<0x111, 0xf>(t), t);  // row_shr:1
+  t = M::combine(M::template dpp<0x112, 0xf>(t), t);  // row_shr:2
+  t = M::combine(M::template dpp<0x114, 0xf>(t), t);  // row_shr:4
+  t = M::combine(M::template dpp<0x118, 0xf>(t), t);  // row_shr:8
+  t = M::combine(M::template dpp<0x142, 0xa>(t), t);  // row_bcast:15 into rows 1 and 3
+  t = M::combine(M::template dpp<0x143, 0xc>(t), t);  // row_bcast:31 into rows 2 and 3
+  return t;
+}
+
+template <bool B>
+struct Full {
+  static constexpr bool value = B;
+};
+
 template <class M, typename T, bool ALIGNED>
-__global__ __launch_bounds__(256) void row_scan_kernel(const T* __restrict__ x, int n,
-                                                     float* __restrict__ out0,
-                                                     float* __restrict__ out1) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void row_scan_kernel(
+    const T* __restrict__ x, int n, float* __restrict__ out0, float* __restrict__ out1) {
   using S = typename M::S;
-  __shared__ S wtot[4];
-  // A whole block's outputs go out through LDS so that every store instruction writes
-  // 1 KB of consecutive floats (a thread's own 8 results are 32 bytes apart per lane).
-  __shared__ __attribute__((aligned(16))) float stage[2][256 * kK];
+  constexpr int VEC = 16 / int(sizeof(T));  // input elements per 16-byte vector
+  constexpr int NIN = kWaveSpan / VEC / 64;  // input vectors per lane per block
+  constexpr int NOUT = kWaveSpan / 4 / 64;   // vectors per lane per block of each output
+  __shared__ S wtot[2][4];                   // wavefront totals, by block parity
+  __shared__ u32x4_t stage[4][kStageVecs];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const T* p = x + row * int64_t(n);
   float* o0 = out0 + row * int64_t(n);
   float* o1 = out1 + row * int64_t(n);
+  u32x4_t* area = stage[wave];
   S carry = M::identity();
-  for (int base = 0; base < n; base += 256 * kK) {
-    const int e0 = base + kK * tid;
-    S st[kK];
-    S run = M::identity();
-    if (ALIGNED && e0 + kK <= n) {
-      float v[kK];
+
+  auto block = [&](auto full, int base, int parity) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full)::value;
+    const int w0 = base + kWaveSpan * wave;  // the wavefront's first element
+    const int e0 = w0 + kOwn * lane;         // the lane's first element
+    float v[kOwn];
+    if (ALIGNED) {
+      u32x4_t raw[NIN];
 #pragma unroll
-      for (int j = 0; j < kK / Elem<T>::kVec; ++j) {
-        float w[Elem<T>::kVec];
-        Elem<T>::vec(p + e0 + j * Elem<T>::kVec, w);
-#pragma unroll
-        for (int i = 0; i < Elem<T>::kVec; ++i) v[j * Elem<T>::kVec + i] = w[i];
+      for (int j = 0; j < NIN; ++j) {
+        const int e = w0 + VEC * (lane + 64 * j);
+        if (FULL || e < n)
+          raw[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + e));
       }
 #pragma unroll
-      for (int i = 0; i < kK; ++i) {
-        run = M::combine(run, M::inject(v[i]));
-        st[i] = run;
+      for (int j = 0; j < NIN; ++j) area[slot(lane + 64 * j)] = raw[j];
+      wave_sync();
+#pragma unroll
+      for (int k = 0; k < NIN; ++k) {
+        const u32x4_t w = area[slot(NIN * lane + k)];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          if constexpr (sizeof(T) == 4)
+            v[VEC * k + i] = __uint_as_float(w[i]);
+          else
+            v[VEC * k + i] = (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
+        }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kK; ++i) {
-        if (e0 + i < n) run = M::combine(run, M::inject(Elem<T>::scalar(p + e0 + i)));
-        st[i] = run;
-      }
+      for (int i = 0; i < kOwn; ++i) v[i] = e0 + i < n ? Elem<T>::scalar(p + e0 + i) : 0.f;
     }
-    // inclusive scan of the thread totals across the wavefront
-    S tot = run;
+    // the lane's total
+    S tot;
+    if (FULL) {
+      tot = M::of_block(v);
+    } else {
+      tot = M::identity();
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const S o = M::shfl_up(tot, off);
-      if (lane >= off) tot = M::combine(o, tot);
+      for (int i = 0; i < kOwn; ++i)
+        if (e0 + i < n) tot = M::push(tot, v[i]);
     }
-    S excl = M::shfl_up(tot, 1);  // totals of the lanes before this one
-    if (lane == 0) excl = M::identity();
-    if (lane == 63) wtot[wave] = tot;
+    tot = wave_inclusive_scan<M>(tot);
+    const S ex = M::template dpp<0x138, 0xf>(tot);  // wave_shr:1, the lanes before
+    if (lane == 0) wtot[parity][wave] = M::readlane(tot, 63);
     __syncthreads();
+    // wtot[parity] is rewritten two blocks later, after every wavefront has passed the
+    // next block's barrier, hence after these reads. The carry followed by the
+    // wavefront totals in order: pre is the state before this wavefront's elements, blk
+    // the state after the whole block.
     S pre = carry, blk = carry;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      if (w < wave) pre = M::combine(pre, wtot[w]);
-      blk = M::combine(blk, wtot[w]);
-    }
-    pre = M::combine(pre, excl);
-    __syncthreads();  // wtot is rewritten by the next block
-    float r0[kK], r1[kK];
-#pragma unroll
-    for (int i = 0; i < kK; ++i) {
-      const S r = M::combine(pre, st[i]);
-      r0[i] = M::first(r);
-      r1[i] = M::second(r);
-    }
-    if (ALIGNED && base + 256 * kK <= n) {  // uniform: the whole block is in the row
-#pragma unroll
-      for (int j = 0; j < kK; j += 4) {
-        *reinterpret_cast<f32x4_t*>(&stage[0][kK * tid + j]) = f32x4_t{r0[j], r0[j + 1], r0[j + 2], r0[j + 3]};
-        *reinterpret_cast<f32x4_t*>(&stage[1][kK * tid + j]) = f32x4_t{r1[j], r1[j + 1], r1[j + 2], r1[j + 3]};
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < kK / 4; ++q) {
-        const int f = 4 * (tid + 256 * q);
-        *reinterpret_cast<f32x4_t*>(o0 + base + f) = *reinterpret_cast<const f32x4_t*>(&stage[0][f]);
-        *reinterpret_cast<f32x4_t*>(o1 + base + f) = *reinterpret_cast<const f32x4_t*>(&stage[1][f]);
-      }
-      // stage is rewritten by the next block only after that block's two barriers
-    } else if (ALIGNED && e0 + kK <= n) {
-#pragma unroll
-      for (int j = 0; j < kK; j += 4) {
-        *reinterpret_cast<f32x4_t*>(o0 + e0 + j) = f32x4_t{r0[j], r0[j + 1], r0[j + 2], r0[j + 3]};
-        *reinterpret_cast<f32x4_t*>(o1 + e0 + j) = f32x4_t{r1[j], r1[j + 1], r1[j + 2], r1[j + 3]};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kK; ++i)
-        if (e0 + i < n) {
-          o0[e0 + i] = r0[i];
-          o1[e0 + i] = r1[i];
-        }
+      if (w == wave) pre = blk;
+      blk = M::combine(blk, wtot[parity][w]);
     }
     carry = blk;
-  }
+    // fold again onto everything before the lane, keeping every position's state
+    S r = M::combine(pre, ex);
+    float r1[kOwn];
+    if (ALIGNED) wave_sync();  // every lane has read its input from the area
+#pragma unroll
+    for (int k = 0; k < kOwn / 4; ++k) {
+      float r0[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (FULL || e0 + 4 * k + i < n) r = M::push(r, v[4 * k + i]);
+        r0[i] = M::first(r);
+        r1[4 * k + i] = M::second(r);
+      }
+      if (ALIGNED)
+        area[slot(NOUT * lane + k)] = __builtin_bit_cast(u32x4_t, f32x4_t{r0[0], r0[1], r0[2], r0[3]});
+      else
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e0 + 4 * k + i < n) o0[e0 + 4 * k + i] = r0[i];
+    }
+    if (ALIGNED) {
+      // the two outputs leave through the area in turn, as 1 KB runs per instruction;
+      // non-temporal: every output is written once and read by no one here
+      auto drain = [&](float* o) __attribute__((always_inline)) {
+        wave_sync();
+        u32x4_t out[NOUT];
+#pragma unroll
+        for (int j = 0; j < NOUT; ++j) out[j] = area[slot(lane + 64 * j)];
+#pragma unroll
+        for (int j = 0; j < NOUT; ++j) {
+          const int e = w0 + 4 * (lane + 64 * j);
+          if (FULL || e < n)
+            __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, out[j]),
+                                        reinterpret_cast<f32x4_t*>(o + e));
+        }
+        wave_sync();
+      };
+      drain(o0);
+#pragma unroll
+      for (int k = 0; k < kOwn / 4; ++k)
+        area[slot(NOUT * lane + k)] =
+            __builtin_bit_cast(u32x4_t, f32x4_t{r1[4 * k], r1[4 * k + 1], r1[4 * k + 2], r1[4 * k + 3]});
+      drain(o1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kOwn; ++i)
+        if (e0 + i < n) o1[e0 + i] = r1[i];
+    }
+  };
+
+  const int nfull = n / kScanBlock;  // blocks wholly inside the row
+  int b = 0;
+  for (; b < nfull; ++b) block(Full<true>(), b * kScanBlock, b & 1);
+  if (b * kScanBlock < n) block(Full<false>(), b * kScanBlock, b & 1);
 }
 
 template <class M, typename T>
@@ -354,7 +507,8 @@ hipError_t launch_scan(const RowReduceArgs& a, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 &&
                        (reinterpret_cast<uintptr_t>(a.out0) & 15) == 0 &&
-                       (reinterpret_cast<uintptr_t>(a.out1) & 15) == 0 && (a.n % kK) == 0;
+                       (reinterpret_cast<uintptr_t>(a.out1) & 15) == 0 &&
+                       (a.n % (16 / int(sizeof(T)))) == 0;
   if (aligned)
     hipLaunchKernelGGL((row_scan_kernel<M, T, true>), dim3(unsigned(a.rows)), dim3(256), 0, st, x,
                        a.n, a.out0, a.out1);

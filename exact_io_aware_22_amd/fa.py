@@ -24,8 +24,9 @@ _lib = None
 FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
-            "fa_decode_noalloc", "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-            "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
+            "fa_decode_noalloc", "fa_backward", "fa_softmax_stats", "fa_moments",
+            "fa_softmax_scan", "fa_moments_scan", "fa_calibrate_mfma", "fa_calibrate_overlap",
+            "fa_calibrate_read", "fa_calibrate_write", "fa_calibrate_mix", "fa_strerror",
             "fa_abi_version")
 
 
@@ -71,6 +72,8 @@ def load():
     lib.fa_calibrate_read.restype = i
     lib.fa_calibrate_write.argtypes = [vp, ctypes.c_longlong, ctypes.c_uint, i, vp]
     lib.fa_calibrate_write.restype = i
+    lib.fa_calibrate_mix.argtypes = [vp, ctypes.c_longlong, vp, i, i, vp]
+    lib.fa_calibrate_mix.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -380,6 +383,21 @@ def fa_calibrate_write(y, value: int, blocks: int, stream=None) -> None:
     code = load().fa_calibrate_write(_ptr(y), nbytes, int(value) & 0xFFFFFFFF, int(blocks),
                                      _stream(stream))
     _check(code, "fa_calibrate_write")
+
+
+def fa_calibrate_mix(x, y, ratio: int, blocks: int, stream=None) -> None:
+    """Measurement only: reads the bytes of x (a multiple of 4096) and writes them to two
+    output streams, each `ratio` times as many bytes, in y (at least 2 * ratio times the
+    bytes of x): the run of 256 16-byte words at word j goes to words ratio j + 256 r + t
+    (word j + t) of both streams."""
+    _dense(x, y)
+    _on_one_device(x=x, y=y)
+    nbytes = x.numel() * x.element_size()
+    if y.numel() * y.element_size() < 2 * int(ratio) * nbytes:
+        raise ValueError("y must hold 2 * ratio times the bytes of x")
+    code = load().fa_calibrate_mix(_ptr(x), nbytes, _ptr(y), int(ratio), int(blocks),
+                                   _stream(stream))
+    _check(code, "fa_calibrate_mix")
 
 
 # ------------------------------------------------------------------ conveniences

@@ -300,6 +300,22 @@ int fa_calibrate_read(const void* x, long long nbytes, unsigned* out, int blocks
  *   y 16-byte aligned. nbytes = 0 returns FA_OK at once (y may then be NULL).
  */
 int fa_calibrate_write(void* y, long long nbytes, unsigned value, int blocks, void* stream);
+/*
+ * fa_calibrate_mix -- one read stream and two write streams, with no arithmetic: the
+ * traffic of a kernel that reads a buffer and writes two outputs `ratio` times its size
+ * (the prefix scans: ratio 1 for float32 input, 2 for bfloat16), so its rate is the
+ * measured ceiling for that mix of reads and writes. `blocks` workgroups of 256 threads
+ * split x[0 .. nbytes) as fa_calibrate_read does and read their 16-byte words with
+ * non-temporal loads; the run of 256 words starting at word j (j a multiple of 256) is
+ * written, with non-temporal stores, to words ratio j + 256 r + t (r < ratio, t < 256:
+ * word j + t) of both output streams. Stream 0 is y[0 .. ratio nbytes), stream 1
+ * y[ratio nbytes .. 2 ratio nbytes).
+ *   nbytes >= 0 and a multiple of 4096, ratio 1, 2 or 4, 1 <= blocks <= 2^22
+ *   (FA_ERR_SHAPE otherwise); x and y 16-byte aligned, y holding 2 ratio nbytes bytes.
+ *   nbytes = 0 returns FA_OK at once (x and y may then be NULL).
+ */
+int fa_calibrate_mix(const void* x, long long nbytes, void* y, int ratio, int blocks,
+                     void* stream);
 
 /* Static, human-readable name of an FA_* code (never NULL). */
 const char* fa_strerror(int code);

@@ -38,8 +38,8 @@ def test_header_declares_the_documented_calls():
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
          "fa_decode_noalloc",
          "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
-         "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_strerror",
-         "fa_abi_version"])
+         "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_calibrate_mix",
+         "fa_strerror", "fa_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -230,6 +230,19 @@ def test_calibration_validation(lib):
     assert wr(P, 1000, 1, 4, None) == SHAPE
     assert wr(P, 1024, 1, 0, None) == SHAPE
     assert wr(P + 8, 1024, 1, 4, None) == ALIGN
+    mx = lib.fa_calibrate_mix
+    assert mx(None, 0, None, 1, 4, None) == OK      # empty: returns before any HIP call
+    assert mx(None, 4096, P, 1, 4, None) == NULL
+    assert mx(P, 4096, None, 2, 4, None) == NULL
+    assert mx(P, 4000, P, 1, 4, None) == SHAPE      # not a multiple of 4096
+    assert mx(P, 2048, P, 1, 4, None) == SHAPE
+    assert mx(P, -4096, P, 1, 4, None) == SHAPE
+    assert mx(P, 4096, P, 3, 4, None) == SHAPE      # ratio 1, 2 or 4 only
+    assert mx(P, 4096, P, 0, 4, None) == SHAPE
+    assert mx(P, 4096, P, 1, 0, None) == SHAPE
+    assert mx(P, 4096, P, 1, (1 << 22) + 1, None) == SHAPE
+    assert mx(P + 8, 4096, P, 1, 4, None) == ALIGN
+    assert mx(P, 4096, P + 4, 1, 4, None) == ALIGN
 
 
 

@@ -1,6 +1,7 @@
-"""The measurement calls (fa_calibrate_read, fa_calibrate_mfma) through the C ABI on one
-MI355X: the read stream's per-thread XOR is checked against the same fold computed on
-the host; the MFMA loop is checked for finite, seed-determined checksums."""
+"""The measurement calls (fa_calibrate_read, _write, _mix, _mfma, _overlap) through the C
+ABI on one MI355X: the read stream's per-thread XOR is checked against the same fold
+computed on the host, the write and mix streams' outputs word by word, the MFMA loop
+for finite, seed-determined checksums, the overlap probe for its placement."""
 import numpy as np
 import pytest
 import torch
@@ -74,6 +75,25 @@ def test_write_stream_pattern(n16, blocks):
                      np.full(n16, 0x5EED1234, np.uint32), w], axis=1).reshape(-1)
     assert np.array_equal(got[:4 * n16], want)
     assert not got[4 * n16:].any()  # nothing past the end
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 4])
+@pytest.mark.parametrize("n16,blocks", [(256, 1), (256, 3), (256 * 37, 5), (1 << 18, 64)])
+def test_mix_stream_pattern(n16, blocks, ratio):
+    """fa_calibrate_mix: both output streams hold every input word `ratio` times, run by
+    run (the run of 256 words at j in words ratio j + 256 r + t), and nothing past them
+    is written; spans with an odd number of runs and workgroups with none included."""
+    print(f"calibrate_mix n16={n16} blocks={blocks} ratio={ratio}", flush=True)
+    x = torch.randint(-2**31, 2**31 - 1, (4 * n16,), dtype=torch.int32, device="cuda")
+    y = torch.zeros(2 * ratio * 4 * n16 + 8, dtype=torch.int32, device="cuda")
+    fa.fa_calibrate_mix(x, y[:2 * ratio * 4 * n16], ratio, blocks)
+    torch.cuda.synchronize()
+    xs = x.cpu().numpy().reshape(-1, 256, 4)                    # runs of 256 words
+    want = np.repeat(xs[:, None], ratio, axis=1).reshape(-1)    # run j: ratio copies
+    got = y.cpu().numpy()
+    n = ratio * 4 * n16
+    assert np.array_equal(got[:n], want) and np.array_equal(got[n:2 * n], want)
+    assert not got[2 * n:].any()
 
 
 def test_overlap_probe_placement_and_checksums():

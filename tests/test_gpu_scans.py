@@ -2,9 +2,10 @@
 the fp64 oracle, on one MI355X.
 
 Tolerances, from the kernel's float32 arithmetic (u = 2^-24): the state written at
-position j is the end of a chain of at most 8 (a thread's own elements) + 6 (the scan
-across a wavefront) + 4 (the wavefront totals) + n / 2048 (the carry from earlier
-blocks) + 2 combines, each a few roundings (one hardware exp2 per rescale). Hence
+position j is the end of a chain of at most 8 (a lane's own elements) + 6 (the scan
+across a wavefront) + 1 (the lanes before) + 4 (the wavefront totals) + n / 2048 (the
+carry from earlier blocks) + 2 combines, each a few roundings (one hardware exp2 per
+rescale). Hence
 * m: exact (a running maximum of the inputs);
 * d: relative (n / 2048 + 32) * 4u;
 * mean: absolute (n / 2048 + 32) * 4u * max|x|;
