@@ -232,8 +232,20 @@ __global__ __launch_bounds__(kReadThreads) void write_stream_kernel(u32x4_t* __r
 }
 
 // Workgroup b reads its span (the read stream's split, whole runs of 256 words) two
-// runs at a time, and writes the run of 256 words at j to words ratio j + 256 r + t
-// (r < ratio) of both output streams: every store instruction is one contiguous run.
+// runs at a time, both loads in flight before the stores, and writes the run of 256
+// words at j to words ratio j + 256 r + t (r < ratio) of both output streams: every
+// store instruction is one contiguous run.
+template <int RATIO>
+__device__ __forceinline__ void mix_store(u32x4_t v, int64_t j, int t, u32x4_t* __restrict__ y0,
+                                          u32x4_t* __restrict__ y1) {
+#pragma unroll
+  for (int r = 0; r < RATIO; ++r) {
+    const int64_t o = RATIO * j + kReadThreads * r + t;
+    __builtin_nontemporal_store(v, y0 + o);
+    __builtin_nontemporal_store(v, y1 + o);
+  }
+}
+
 template <int RATIO>
 __global__ __launch_bounds__(kReadThreads) void mix_stream_kernel(const u32x4_t* __restrict__ x,
                                                                    int64_t n16, int64_t span,
@@ -242,26 +254,14 @@ __global__ __launch_bounds__(kReadThreads) void mix_stream_kernel(const u32x4_t*
   const int64_t b0 = int64_t(blockIdx.x) * span;
   const int64_t end = min(n16, b0 + span);  // a multiple of 256: n16 and span are
   const int t = threadIdx.x;
-  for (int64_t j = b0; j < end; j += 2 * kReadThreads) {
-    const bool two = j + kReadThreads < end;  // uniform
+  int64_t j = b0;
+  for (; j + kReadThreads < end; j += 2 * kReadThreads) {
     const u32x4_t v0 = __builtin_nontemporal_load(x + j + t);
-    u32x4_t v1 = {};
-    if (two) v1 = __builtin_nontemporal_load(x + j + kReadThreads + t);
-#pragma unroll
-    for (int r = 0; r < RATIO; ++r) {
-      const int64_t o = RATIO * j + kReadThreads * r + t;
-      __builtin_nontemporal_store(v0, y0 + o);
-      __builtin_nontemporal_store(v0, y1 + o);
-    }
-    if (two) {
-#pragma unroll
-      for (int r = 0; r < RATIO; ++r) {
-        const int64_t o = RATIO * (j + kReadThreads) + kReadThreads * r + t;
-        __builtin_nontemporal_store(v1, y0 + o);
-        __builtin_nontemporal_store(v1, y1 + o);
-      }
-    }
+    const u32x4_t v1 = __builtin_nontemporal_load(x + j + kReadThreads + t);
+    mix_store<RATIO>(v0, j, t, y0, y1);
+    mix_store<RATIO>(v1, j + kReadThreads, t, y0, y1);
   }
+  if (j < end) mix_store<RATIO>(__builtin_nontemporal_load(x + j + t), j, t, y0, y1);
 }
 
 }  // namespace
