@@ -18,10 +18,10 @@
 //     from LDS), P^T and dS^T element-wise (one lse and one Delta per lane), then
 //     dQ^T += K^T dS^T with K^T read by the transposing LDS read.
 //   * dkdv_kernel: a wavefront owns 32 key rows (K^T and V^T fragments in registers)
-//     and walks the query tiles: S = Q K^T and dP = dO V^T (A operands: Q and dO rows
-//     from LDS), P and dS element-wise (16 queries per lane, their lse and Delta read
-//     from LDS), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by the
-//     transposing LDS read.
+//     and walks the query tiles, each 32-query block as one chain: S = Q K^T (A
+//     operand: Q rows from LDS), P element-wise (16 queries per lane, their lse read
+//     from LDS), dV^T += dO^T P (dO^T by the transposing LDS read); then dP = dO V^T,
+//     dS = P (dP - Delta) from the bf16 P the dV product used, dK^T += Q^T dS.
 // Every product is v_mfma_f32_32x32x16_bf16; the element-wise results a lane holds
 // are, after bf16 packing, exactly the B operand of the next product (the swap23 row
 // order used by the forward kernel). A tile read both row-wise (16-byte reads) and
@@ -30,8 +30,8 @@
 // free of bank conflicts on 64 banks, and no single padding serves both.
 // Staging: both kernels load their 64-row tiles by direct global -> LDS loads, each
 // tile into every layout it is read in, so no registers hold staged data (dq_kernel:
-// K and V, 8 wavefronts, 256 query rows; dkdv_kernel: Q and dO, 8 wavefronts at D = 64,
-// 4 at D = 128). Two LDS slots, one barrier per tile.
+// K and V, 8 wavefronts, 256 query rows; dkdv_kernel: Q and dO, 8 wavefronts, 256 key
+// rows). Two LDS slots, one barrier per tile.
 #include <type_traits>
 
 #include "device.h"
@@ -40,13 +40,13 @@
 namespace fa {
 namespace {
 
-// dK/dV: wavefronts per workgroup. At D = 64 eight (two per SIMD: one's element-wise
-// work overlaps the other's products); at D = 128 the two 32 x 128 accumulators and the
-// own K^T, V^T fragments leave too few of 256 VGPRs (it spills), so four (one per SIMD,
-// up to 512 registers).
+// dK/dV: eight wavefronts per workgroup, two per SIMD, so one's element-wise work
+// overlaps the other's products. At D = 128 that leaves 256 registers per wavefront for
+// the two 32 x 128 accumulators (128), the own K^T and V^T fragments (64) and one 32 x 32
+// product at a time: S and dP are formed one after the other, never both live.
 template <int D>
 struct KV {
-  static constexpr int kWaves = D == 64 ? 8 : 4;
+  static constexpr int kWaves = 8;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kRows = 32 * kWaves;  // key rows a workgroup owns
 };
@@ -390,36 +390,21 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   };
   const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
 
-  // Block g (32 queries) of the tile in slot s, in three phases: S and dP (MFMA), P and
-  // dS element-wise (VALU), then dV^T and dK^T (MFMA).
-  auto sdp = [&](int g, const uint8_t* s, f32x16_t& st, f32x16_t& dp) __attribute__((always_inline)) {
-    const int b = (g & 1) * 32;
-    const uint8_t* qr = s + b * G::RS + roff;
-    const uint8_t* dr = s + G::RT + G::CT + b * G::RS + roff;
-    st = f32x16_t{};
-    dp = f32x16_t{};
-#pragma unroll
-    for (int c2 = 0; c2 < G::NCH; ++c2) {
-      st = mfma(frag_row(qr, c2), as_bf16x8(kf[c2]), st);
-      dp = mfma(frag_row(dr, c2), as_bf16x8(vf[c2]), dp);
-    }
-  };
   // Registers 8 cc + 4 h4 + k hold query 32 g + 16 cc + 8 half + 4 h4 + k: each group
-  // of four reads its four lse and Delta values just before use.
-  // `masked` is a std::integral_constant: unmasked blocks carry no mask arithmetic.
-  auto ew = [&](int g, const uint8_t* s, const f32x16_t& st, const f32x16_t& dp, auto masked,
-                uint32_t (&pk)[8], uint32_t (&dsk)[8]) __attribute__((always_inline)) {
+  // of four reads its four lse (P) or Delta (dS) values just before use.
+  // P of block g, packed to bf16; `masked` is a std::integral_constant: unmasked blocks
+  // carry no mask arithmetic.
+  auto ew_p = [&](int g, const uint8_t* s, const f32x16_t& st, auto masked, uint32_t (&pk)[8])
+      __attribute__((always_inline)) {
     const float* fl = reinterpret_cast<const float*>(s + 2 * G::RT + 2 * G::CT) + (g & 1) * 32;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int h4 = 0; h4 < 2; ++h4) {
         const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(fl + 16 * cc + 8 * half + 4 * h4);
-        const f32x4_t d4 =
-            *reinterpret_cast<const f32x4_t*>(fl + kTile + 16 * cc + 8 * half + 4 * h4);
 #pragma unroll
         for (int k2 = 0; k2 < 4; k2 += 2) {
-          float pv[2], dv2[2];
+          float pv[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int k = k2 + e, r = 8 * cc + 4 * h4 + k;
@@ -427,41 +412,71 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
             float sv = st[r];
             if (decltype(masked)::value && (q >= N || (CAUSAL && krow > q))) sv = kNegInf;
             pv[e] = exp2_hw(fmaf(sv, c, -l4[k]));
-            dv2[e] = pv[e] * (dp[r] - d4[k]);
           }
-          const int i = (8 * cc + 4 * h4 + k2) >> 1;
-          pk[i] = pack_bf16x2(pv[0], pv[1]);
-          dsk[i] = pack_bf16x2(dv2[0], dv2[1]);
+          pk[(8 * cc + 4 * h4 + k2) >> 1] = pack_bf16x2(pv[0], pv[1]);
         }
       }
   };
-  auto acc = [&](int g, const uint8_t* s, const uint32_t (&pk)[8], const uint32_t (&dsk)[8]) __attribute__((always_inline)) {
-    const int b = (g & 1) * 32;
-    const uint8_t* qt = s + G::RT + b * G::CS + toff;
-    const uint8_t* dt = s + 2 * G::RT + G::CT + b * G::CS + toff;
+  // dS = P (dP - Delta) of block g from the packed P (the values the dV product used);
+  // masked entries have P = 0, so dS needs no mask.
+  auto ew_ds = [&](int g, const uint8_t* s, const f32x16_t& dp, const uint32_t (&pk)[8],
+                   uint32_t (&dsk)[8]) __attribute__((always_inline)) {
+    const float* fd =
+        reinterpret_cast<const float*>(s + 2 * G::RT + 2 * G::CT) + kTile + (g & 1) * 32;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(fd + 16 * cc + 8 * half + 4 * h4);
+#pragma unroll
+        for (int k2 = 0; k2 < 4; k2 += 2) {
+          const int r = 8 * cc + 4 * h4 + k2, i = r >> 1;
+          dsk[i] = pack_bf16x2(bf16_lo(pk[i]) * (dp[r] - d4[k2]),
+                               bf16_hi(pk[i]) * (dp[r + 1] - d4[k2 + 1]));
+        }
+      }
+  };
+  // dV^T += dO^T P or dK^T += Q^T dS for block g (transposing reads of the tile).
+  auto tr_product = [&](int g, const uint8_t* tb0, const uint32_t (&b)[8], f32x16_t (&acc)[G::NDB])
+      __attribute__((always_inline)) {
+    const uint8_t* tb = tb0 + (g & 1) * 32 * G::CS + toff;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      const u32x4_t bp = {pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]};
-      const u32x4_t bs = {dsk[4 * cc], dsk[4 * cc + 1], dsk[4 * cc + 2], dsk[4 * cc + 3]};
+      const u32x4_t bop = {b[4 * cc], b[4 * cc + 1], b[4 * cc + 2], b[4 * cc + 3]};
 #pragma unroll
-      for (int db = 0; db < G::NDB; ++db) {
-        dva[db] = mfma(frag_tr(dt, cc, db, G::CS), as_bf16x8(bp), dva[db]);
-        dka[db] = mfma(frag_tr(qt, cc, db, G::CS), as_bf16x8(bs), dka[db]);
-      }
+      for (int db = 0; db < G::NDB; ++db)
+        acc[db] = mfma(frag_tr(tb, cc, db, G::CS), as_bf16x8(bop), acc[db]);
     }
   };
-  // One block: the diagonal and ragged blocks (queries past N, or below a key of this
-  // wavefront under the causal mask) take the masked variant, every other block one
-  // with no mask arithmetic.
+  // S = Q K^T or dP = dO V^T of block g (row reads of the tile, own fragments).
+  auto rows_product = [&](int g, const uint8_t* rb0, const u32x4_t (&own)[G::NCH], f32x16_t& out)
+      __attribute__((always_inline)) {
+    const uint8_t* r = rb0 + (g & 1) * 32 * G::RS + roff;
+    out = f32x16_t{};
+#pragma unroll
+    for (int c2 = 0; c2 < G::NCH; ++c2) out = mfma(frag_row(r, c2), as_bf16x8(own[c2]), out);
+  };
+  // One block, one chain: S, P, dV^T, then dP, dS, dK^T, so S and dP are never live at
+  // once (with both 32 x D accumulators and the own K^T, V^T fragments this fits the 256
+  // registers of two wavefronts per SIMD). The diagonal and ragged blocks (queries past
+  // N, or below a key of this wavefront under the causal mask) take the masked P.
   auto step = [&](int g, const uint8_t* s) __attribute__((always_inline)) {
-    f32x16_t st, dp;
     uint32_t pk[8], dsk[8];
-    sdp(g, s, st, dp);
-    if ((32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32))
-      ew(g, s, st, dp, std::true_type{}, pk, dsk);
-    else
-      ew(g, s, st, dp, std::false_type{}, pk, dsk);
-    acc(g, s, pk, dsk);
+    {
+      f32x16_t st;
+      rows_product(g, s, kf, st);
+      if ((32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32))
+        ew_p(g, s, st, std::true_type{}, pk);
+      else
+        ew_p(g, s, st, std::false_type{}, pk);
+    }
+    tr_product(g, s + 2 * G::RT + G::CT, pk, dva);
+    {
+      f32x16_t dp;
+      rows_product(g, s + G::RT + G::CT, vf, dp);
+      ew_ds(g, s, dp, pk, dsk);
+    }
+    tr_product(g, s + G::RT, dsk, dka);
   };
 
   const int ntiles = k0 >= N ? 0 : ntiles_all - t_first;
