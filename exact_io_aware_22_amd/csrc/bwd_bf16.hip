@@ -121,11 +121,18 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, const uint8_t* reg
       (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
   const bool ragged = t * kTile + kTile > N;
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(const uint8_t, region)));
+  // At D = 128 the per-lane offsets are recomputed at every call (a few instructions
+  // each) rather than kept across the tile loop: `lane` passes through an empty asm
+  // statement, so the compiler cannot hoist them into registers the products need (kept,
+  // they pushed the dK/dV kernel past 256 registers, and a spilled offset reloaded
+  // between two staging loads waited for all loads in flight).
+  int ln = lane;
+  if constexpr (D == 128) asm volatile("" : "+v"(ln));
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int j = wave + WAVES * i;
     if (j < C) {
-      const int p = 64 * j + lane, r = p / C, col = min(p % C, CPR - 1);
+      const int p = 64 * j + ln, r = p / C, col = min(p % C, CPR - 1);
       const int row = ragged ? min(t * kTile + r, N - 1) - t * kTile : r;
       const uint32_t off = uint32_t(row << kRowShift) + uint32_t(col * 16);
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
