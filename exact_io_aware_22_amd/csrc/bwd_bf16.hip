@@ -121,13 +121,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, const uint8_t* reg
       (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
   const bool ragged = t * kTile + kTile > N;
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(const uint8_t, region)));
-  // At D = 128 the per-lane offsets are recomputed at every call (a few instructions
-  // each) rather than kept across the tile loop: `lane` passes through an empty asm
-  // statement, so the compiler cannot hoist them into registers the products need (kept,
-  // they pushed the dK/dV kernel past 256 registers, and a spilled offset reloaded
-  // between two staging loads waited for all loads in flight).
-  int ln = lane;
-  if constexpr (D == 128) asm volatile("" : "+v"(ln));
+  const int ln = lane;
 #pragma unroll
   for (int i = 0; i < MAXI; ++i) {
     const int j = wave + WAVES * i;
@@ -142,6 +136,17 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, const uint8_t* reg
                    : "memory");
     }
   }
+}
+// The lane index as the staging calls of one tile see it. At D = 128 it passes through
+// an empty asm statement once per tile, so the per-lane staging offsets are recomputed
+// for each tile (a few instructions, shared by the tile's calls of one layout) rather
+// than kept across the tile loop in registers the products need: kept, they pushed the
+// dK/dV kernel past 256 registers, and a spilled offset reloaded between two staging
+// loads waited for every load in flight.
+template <int D>
+__device__ __forceinline__ int staging_lane(int lane) {
+  if constexpr (D == 128) asm volatile("" : "+v"(lane));
+  return lane;
 }
 // s_waitcnt vmcnt(0), through the builtin so the compiler's own bookkeeping sees it.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -247,9 +252,10 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
   static_assert(G::RT == CR * 1024 && G::CT == CC * 1024, "a padded tile is C kilobytes");
   auto gload = [&](int t, int slot) __attribute__((always_inline)) {
     const uint8_t* s = smem + slot * SLOT;
-    dma_tile<D, CR, kWavesQ>(Kh, s, t, N, wave, lane);
-    dma_tile<D, CC, kWavesQ>(Kh, s + G::RT, t, N, wave, lane);
-    dma_tile<D, CR, kWavesQ>(Vh, s + G::RT + G::CT, t, N, wave, lane);
+    const int sl = staging_lane<D>(lane);
+    dma_tile<D, CR, kWavesQ>(Kh, s, t, N, wave, sl);
+    dma_tile<D, CC, kWavesQ>(Kh, s + G::RT, t, N, wave, sl);
+    dma_tile<D, CR, kWavesQ>(Vh, s + G::RT + G::CT, t, N, wave, sl);
   };
   const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
   const int first_masked = CAUSAL ? min(N >> 5, qw0 >> 5) : (N >> 5);
@@ -376,10 +382,11 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   float sl = 0.f, sdl = 0.f;
   auto gload = [&](int t, int slot) __attribute__((always_inline)) {
     const uint8_t* s = smem + slot * SLOT;
-    dma_tile<D, CR, kWavesB>(Qh, s, t, N, wave, lane);
-    dma_tile<D, CC, kWavesB>(Qh, s + G::RT, t, N, wave, lane);
-    dma_tile<D, CR, kWavesB>(dOh, s + G::RT + G::CT, t, N, wave, lane);
-    dma_tile<D, CC, kWavesB>(dOh, s + 2 * G::RT + G::CT, t, N, wave, lane);
+    const int stl = staging_lane<D>(lane);
+    dma_tile<D, CR, kWavesB>(Qh, s, t, N, wave, stl);
+    dma_tile<D, CC, kWavesB>(Qh, s + G::RT, t, N, wave, stl);
+    dma_tile<D, CR, kWavesB>(dOh, s + G::RT + G::CT, t, N, wave, stl);
+    dma_tile<D, CC, kWavesB>(dOh, s + 2 * G::RT + G::CT, t, N, wave, stl);
     if (tid < kTile) {
       const int q = t * kTile + tid;
       const float l = q < N ? lseh[q] : kNegInf;
