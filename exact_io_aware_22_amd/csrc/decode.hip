@@ -279,11 +279,12 @@ hipError_t launch_partials(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One workgroup of 256 threads per row: thread t owns head dim t mod D of group t / D;
-// the groups split the partials between them. First the row's maximum (every thread
-// strides over the partials' m, then a workgroup reduction), then each group folds its
-// partials with weights e^{m_s - M}, four partials in flight per thread, and the
-// groups' sums are added in LDS. Identity partials (m = -inf) contribute nothing.
+// One workgroup of 256 threads per row: thread t owns the four head dims 4 (t mod D/4)
+// .. + 3 of group t / (D/4); the groups split the partials between them. First the
+// row's maximum (every thread strides over the partials' m, then a workgroup
+// reduction), then each group folds its partials with weights e^{m_s - M}, four
+// 16-byte partial pieces in flight per thread, and the groups' sums are added in LDS.
+// Identity partials (m = -inf) contribute nothing.
 constexpr int kCombineThreads = 256;
 
 template <int D>
@@ -293,15 +294,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
                                                                  float* __restrict__ O,
                                                                  float* __restrict__ LSE,
                                                                  int splits) {
-  constexpr int G = kCombineThreads / D;  // groups of partials
+  constexpr int TPR = D / 4;                  // threads per partial (four floats each)
+  constexpr int G = kCombineThreads / TPR;    // groups of partials
   __shared__ float red[kCombineThreads / 64];
-  __shared__ float acc_s[G][D], den_s[G];
+  __shared__ f32x4_t acc_s[G][TPR];
+  __shared__ float den_s[G];
   const int64_t r = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int dd = t % D, g = t / D;
+  const int q = t % TPR, g = t / TPR;
   const float* mr = M + r * splits;
   const float* dr = Dn + r * splits;
-  const float* orow = Op + r * splits * D + dd;
+  const f32x4_t* orow = reinterpret_cast<const f32x4_t*>(Op + r * splits * D) + q;
 
   float mx = kNegInf;
   for (int s = t; s < splits; s += kCombineThreads) mx = fmaxf(mx, mr[s]);
@@ -313,43 +316,47 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
   for (int w = 0; w < kCombineThreads / 64; ++w) mx = fmaxf(mx, red[w]);
   const float mref = mx == kNegInf ? 0.f : mx;
 
-  float den = 0.f, acc = 0.f;
+  float den = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto fold = [&](float ms, float ds, f32x4_t os) __attribute__((always_inline)) {
+    if (ms == kNegInf) return;  // the identity contributes nothing
+    const float f = exp2_hw((ms - mref) * kLog2e);
+    den = fmaf(f, ds, den);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(f, os[i], acc[i]);
+  };
   int s = g;
   for (; s + 3 * G < splits; s += 4 * G) {
-    float ms[4], ds[4], os[4];
+    float ms[4], ds[4];
+    f32x4_t os[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ms[u] = mr[s + u * G];
       ds[u] = dr[s + u * G];
-      os[u] = orow[int64_t(s + u * G) * D];
+      os[u] = orow[int64_t(s + u * G) * TPR];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (ms[u] == kNegInf) continue;  // the identity contributes nothing
-      const float f = exp2_hw((ms[u] - mref) * kLog2e);
-      den = fmaf(f, ds[u], den);
-      acc = fmaf(f, os[u], acc);
-    }
+    for (int u = 0; u < 4; ++u) fold(ms[u], ds[u], os[u]);
   }
-  for (; s < splits; s += G) {
-    const float ms = mr[s];
-    if (ms == kNegInf) continue;
-    const float f = exp2_hw((ms - mref) * kLog2e);
-    den = fmaf(f, dr[s], den);
-    acc = fmaf(f, orow[int64_t(s) * D], acc);
-  }
-  acc_s[g][dd] = acc;
-  if (dd == 0) den_s[g] = den;
+  for (; s < splits; s += G) fold(mr[s], dr[s], orow[int64_t(s) * TPR]);
+  acc_s[g][q] = acc;
+  if (q == 0) den_s[g] = den;
   __syncthreads();
   if (g == 0) {
-    float a = acc, dn = den;
+    f32x4_t a = acc;
+    float dn = den;
 #pragma unroll
     for (int h = 1; h < G; ++h) {
-      a += acc_s[h][dd];
+      const f32x4_t o = acc_s[h][q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] += o[i];
       dn += den_s[h];
     }
-    O[r * D + dd] = dn > 0.f ? a / dn : 0.f;
-    if (dd == 0) LSE[r] = dn > 0.f ? mx + logf(dn) : kNegInf;
+    f32x4_t out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = dn > 0.f ? a[i] / dn : 0.f;
+    *reinterpret_cast<f32x4_t*>(O + r * D + 4 * q) = out;
+    if (q == 0) LSE[r] = dn > 0.f ? mx + logf(dn) : kNegInf;
   }
 }
 
