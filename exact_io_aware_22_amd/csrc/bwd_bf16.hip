@@ -11,12 +11,13 @@
 //   dS = P (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
 // Masked keys have P = 0 and contribute nothing.
 //
-// Three kernels:
-//   * delta_kernel: Delta_i from dO (bf16) and the forward's O (fp32), 16 lanes per row.
+// Two kernels, dQ first:
 //   * dq_kernel: a wavefront owns 32 query rows (Q^T and dO^T fragments in registers)
-//     and walks the key tiles: S^T = K Q^T and dP^T = V dO^T (A operands: K and V rows
-//     from LDS), P^T and dS^T element-wise (one lse and one Delta per lane), then
-//     dQ^T += K^T dS^T with K^T read by the transposing LDS read.
+//     and first forms its rows' Delta from those dO values and the forward's O (fp32),
+//     writing it for the dK/dV kernel; then it walks the key tiles: S^T = K Q^T and
+//     dP^T = V dO^T (A operands: K and V rows from LDS), P^T and dS^T element-wise (one
+//     lse and one Delta per lane), then dQ^T += K^T dS^T with K^T read by the
+//     transposing LDS read.
 //   * dkdv_kernel: a wavefront owns 32 key rows (K^T and V^T fragments in registers)
 //     and walks the query tiles, each 32-query block as one chain: S = Q K^T (A
 //     operand: Q rows from LDS), P element-wise (16 queries per lane, their lse read
@@ -167,38 +168,13 @@ __device__ __forceinline__ void map_bwd(int bid, int BH, int ntile, bool causal,
   if (causal && heavy_last) t = ntile - 1 - t;
 }
 
-// ------------------------------------------------------------------ Delta
-// Delta_i = sum_d dO_id O_id; 16 lanes per row, D / 16 elements per lane.
-template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ dO,
-                                                    const float* __restrict__ O,
-                                                    float* __restrict__ delta, int64_t rows) {
-  constexpr int E = D / 16;
-  const int64_t row = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int part = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint16_t* g = dO + row * D + part * E;
-    const float* o = O + row * D + part * E;
-#pragma unroll
-    for (int e = 0; e < E; e += 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(g + e);
-      acc = fmaf(bf16_lo(w), o[e], acc);
-      acc = fmaf(bf16_hi(w), o[e + 1], acc);
-    }
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (row < rows && part == 0) delta[row] = acc;
-}
-
 // ------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ dQ,
-    int N, int BH, int nqt, float c, float scale) {
+    const float* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ DELTA,
+    float* __restrict__ dQ, int N, int BH, int nqt, float c, float scale) {
   using G = BGeo<D>;
   constexpr int SLOT = 2 * G::RT + G::CT;  // K rows, K transposing copy, V rows
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
@@ -218,20 +194,41 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
   const int nblk_wg = CAUSAL ? min(nblk_all, ((min(N, q0 + kRowsQ) - 1) >> 5) + 1) : nblk_all;
   const int ntiles = (nblk_wg + 1) >> 1;
 
-  // Own rows: Q^T and dO^T as B operands (k = head dims 16 c2 + 8 half + 0..7).
+  // Own rows: Q^T and dO^T as B operands (k = head dims 16 c2 + 8 half + 0..7). Delta of
+  // the row, dO . O, is formed here from the same dO values and the matching O values
+  // (the two halves of the row's head dims sit in lanes l and l ^ 32) and written for
+  // the dK/dV kernel.
   u32x4_t qf[G::NCH], df[G::NCH];
   float lse2 = kInfB, dl = 0.f;
   {
     const bool ok = qrow < N;
+    const int64_t rowoff = head + int64_t(qrow) * D + 8 * half;
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) {
-      qf[c2] = ok ? load16(Q + head + int64_t(qrow) * D + 16 * c2 + 8 * half) : u32x4_t{0, 0, 0, 0};
-      df[c2] = ok ? load16(dO + head + int64_t(qrow) * D + 16 * c2 + 8 * half) : u32x4_t{0, 0, 0, 0};
+      qf[c2] = ok ? load16(Q + rowoff + 16 * c2) : u32x4_t{0, 0, 0, 0};
+      df[c2] = ok ? load16(dO + rowoff + 16 * c2) : u32x4_t{0, 0, 0, 0};
     }
+    float part = 0.f;
+    if (ok) {
+#pragma unroll
+      for (int c2 = 0; c2 < G::NCH; ++c2) {
+        const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(O + rowoff + 16 * c2);
+        const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(O + rowoff + 16 * c2 + 4);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          part = fmaf(bf16_lo(df[c2][i]), o0[2 * i], part);
+          part = fmaf(bf16_hi(df[c2][i]), o0[2 * i + 1], part);
+          part = fmaf(bf16_lo(df[c2][2 + i]), o1[2 * i], part);
+          part = fmaf(bf16_hi(df[c2][2 + i]), o1[2 * i + 1], part);
+        }
+      }
+    }
+    const float delta_row = part + __shfl_xor(part, 32);
     if (ok) {
       const float l = LSE[int64_t(bh) * N + qrow];
       lse2 = l == kNegInf ? kInfB : l * kLog2e;  // a row that sees no key gets P = 0
-      dl = DELTA[int64_t(bh) * N + qrow];
+      dl = delta_row;
+      if (half == 0) DELTA[int64_t(bh) * N + qrow] = dl;
     }
   }
   f32x16_t acc[G::NDB];
@@ -535,23 +532,18 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
-  const int64_t rows = int64_t(BH) * a.N;
   const float c = a.scale * kLog2e;
   const auto* q = static_cast<const uint16_t*>(a.q);
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
-  const int64_t dblocks = (rows + 15) / 16;
   const int nt = (a.N + KV<D>::kRows - 1) / KV<D>::kRows, ntq = (a.N + kRowsQ - 1) / kRowsQ;
   const int64_t blocks = int64_t(BH) * nt, qblocks = int64_t(BH) * ntq;
-  if (dblocks > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((delta_kernel<D>), dim3(unsigned(dblocks)), dim3(256), 0, s, dout, a.o,
-                     a.delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (qblocks > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // dQ first: it also writes Delta, which the dK/dV kernel reads
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(unsigned(qblocks)), dim3(kThreadsQ), 0, s, q,
-                     k, v, dout, a.lse, a.delta, a.dq, a.N, BH, ntq, c, a.scale);
-  e = hipGetLastError();
+                     k, v, dout, a.o, a.lse, a.delta, a.dq, a.N, BH, ntq, c, a.scale);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(KV<D>::kThreads), 0, s, q,
                      k, v, dout, a.lse, a.delta, a.dk, a.dv, a.N, BH, nt, c, a.scale);
