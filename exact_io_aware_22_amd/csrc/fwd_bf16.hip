@@ -71,8 +71,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per LDS tile (two 32-key blocks)
 constexpr int kSlots = 3;         // LDS ring depth for K and for V
-constexpr float kTau = 32.0f;     // rescale when the maximum grows by more than 2^32
-constexpr float kSumLimit = 4294967296.0f;  // 2^kTau
+constexpr int kTau = 32;          // rescale when the maximum grows by more than 2^32
+constexpr float kSumLimit = float(1ull << kTau);  // 2^kTau
 constexpr float kInf = __builtin_inff();
 
 // Row r of a 32-row K operand block holds key swap23(r): bits 2 and 3 exchanged.
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   constexpr int MAXI = (CV + kWaves - 1) / kWaves;            // loads per wave per tile
   static_assert(CK <= CV && G::KTILE == CK * 1024 && G::VTILE == CV * 1024, "tile = C KB");
   // Source offset (bytes from the tile base) of lane's chunk of kilobyte j in a full tile.
-  auto chunk_off = [&](int j, int C) -> uint32_t __attribute__((always_inline)) {
+  auto chunk_off = [&](int j, int C) __attribute__((always_inline)) -> uint32_t {
     const int p = 64 * j + lane, r = p / C, col = min(p % C, G::CPR - 1);
     return uint32_t(r * D * 2 + col * 16);
   };
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   }
   // The same chunk in tile t when rows past N - 1 are redirected to row N - 1 (its row
   // is off / (2D), a power-of-two division).
-  auto clamp_off = [&](uint32_t off, int t) -> uint32_t __attribute__((always_inline)) {
+  auto clamp_off = [&](uint32_t off, int t) __attribute__((always_inline)) -> uint32_t {
     constexpr int kRowShift = __builtin_ctz(2 * D);
     const int r = int(off >> kRowShift);
     return off - uint32_t((r - (min(t * kBN + r, N - 1) - t * kBN)) << kRowShift);
