@@ -531,22 +531,23 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t s) {
-  const int BH = a.B * a.H;
+  const int64_t BH = int64_t(a.B) * a.H;
   const float c = a.scale * kLog2e;
   const auto* q = static_cast<const uint16_t*>(a.q);
   const auto* k = static_cast<const uint16_t*>(a.k);
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* dout = static_cast<const uint16_t*>(a.dout);
-  const int nt = (a.N + KV<D>::kRows - 1) / KV<D>::kRows, ntq = (a.N + kRowsQ - 1) / kRowsQ;
-  const int64_t blocks = int64_t(BH) * nt, qblocks = int64_t(BH) * ntq;
+  const int nt = int((int64_t(a.N) + KV<D>::kRows - 1) / KV<D>::kRows);
+  const int ntq = int((int64_t(a.N) + kRowsQ - 1) / kRowsQ);
+  const int64_t blocks = BH * nt, qblocks = BH * ntq;
   if (qblocks > 0x7fffffff || blocks > 0x7fffffff) return hipErrorInvalidValue;
   // dQ first: it also writes Delta, which the dK/dV kernel reads
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(unsigned(qblocks)), dim3(kThreadsQ), 0, s, q,
-                     k, v, dout, a.o, a.lse, a.delta, a.dq, a.N, BH, ntq, c, a.scale);
+                     k, v, dout, a.o, a.lse, a.delta, a.dq, a.N, int(BH), ntq, c, a.scale);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(KV<D>::kThreads), 0, s, q,
-                     k, v, dout, a.lse, a.delta, a.dk, a.dv, a.N, BH, nt, c, a.scale);
+                     k, v, dout, a.lse, a.delta, a.dk, a.dv, a.N, int(BH), nt, c, a.scale);
   return hipGetLastError();
 }
 

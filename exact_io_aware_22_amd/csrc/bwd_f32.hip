@@ -110,10 +110,10 @@ __global__ __launch_bounds__(kT) void dkdv_f32_kernel(const float* __restrict__ 
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t s) {
-  const int BH = a.B * a.H;
-  const int64_t rows = int64_t(BH) * a.N;
-  const int nrt = (a.N + kT - 1) / kT;
-  const int64_t blocks = int64_t(BH) * nrt, dblocks = (rows + kT - 1) / kT;
+  const int64_t BH = int64_t(a.B) * a.H;
+  const int64_t rows = BH * a.N;
+  const int nrt = int((int64_t(a.N) + kT - 1) / kT);
+  const int64_t blocks = BH * nrt, dblocks = (rows + kT - 1) / kT;
   if (blocks > 0x7fffffff || dblocks > 0x7fffffff) return hipErrorInvalidValue;
   const float c = a.scale * kLog2e;
   const auto* q = static_cast<const float*>(a.q);

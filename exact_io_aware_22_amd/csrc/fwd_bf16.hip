@@ -543,10 +543,11 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
   // Dense: one unit per (b, h). Packed: one per (sequence, h), B = sequence count.
   const int64_t U = int64_t(a.B) * a.H;
-  const int rows = a.cu_seqlens ? a.max_seqlen : a.N;
-  const int nqt = (rows + kBM - 1) / kBM;
-  const int64_t blocks = U * nqt;
-  if (blocks > 0x7fffffff || U > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t rows = a.cu_seqlens ? a.max_seqlen : a.N;
+  const int nqt = int((rows + kBM - 1) / kBM);
+  if (U > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t blocks = U * nqt;  // < 2^31 * 2^24
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreads), 0,
                      s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),

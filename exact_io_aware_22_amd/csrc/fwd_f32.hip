@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-  const int nqt = (a.N + kQ - 1) / kQ;
+  const int nqt = int((int64_t(a.N) + kQ - 1) / kQ);
   const int64_t blocks = int64_t(a.B) * a.H * nqt;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(unsigned(blocks)), dim3(kThreads), 0, s,
