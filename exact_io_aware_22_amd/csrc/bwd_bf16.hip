@@ -25,14 +25,13 @@
 //     dS = P (dP - Delta) from the bf16 P the dV product used, dK^T += Q^T dS.
 // Every product is v_mfma_f32_32x32x16_bf16; the element-wise results a lane holds
 // are, after bf16 packing, exactly the B operand of the next product (the swap23 row
-// order used by the forward kernel). A tile read both row-wise (16-byte reads) and
-// column-wise (transposing reads) is stored twice in LDS, with +16-byte rows for the
-// former and +64-byte rows for the latter: each padding keeps its own read pattern
-// free of bank conflicts on 64 banks, and no single padding serves both.
-// Staging: both kernels load their 64-row tiles by direct global -> LDS loads, each
-// tile into every layout it is read in, so no registers hold staged data (dq_kernel:
-// K and V, 8 wavefronts, 256 query rows; dkdv_kernel: Q and dO, 8 wavefronts, 256 key
-// rows). Two LDS slots, one barrier per tile.
+// order used by the forward kernel). A tile is read both row-wise (16-byte reads) and
+// column-wise (transposing reads) from one LDS copy whose rows are padded so that
+// neither pattern meets a bank conflict (BGeo below).
+// Staging: both kernels load their 64-row tiles by direct global -> LDS loads, so no
+// registers hold staged data (dq_kernel: K and V, 8 wavefronts, 256 query rows;
+// dkdv_kernel: Q and dO, 8 wavefronts, 256 key rows). Two LDS slots, one barrier per
+// tile.
 #include <type_traits>
 
 #include "device.h"
@@ -63,26 +62,40 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 // lane's accumulator registers 8c..8c+7 hold 8 consecutive rows 16c + 8 half + i.
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// LDS banks: 64 of 4 bytes, served 16 lanes at a time. Sixteen lanes of a 16-byte row
+// read hit 16 different rows at one column (16-byte windows); sixteen lanes of a
+// transposing read hit 4 consecutive rows, 32 bytes each. Either is conflict-free iff
+// its windows, placed at multiples of the row stride, are disjoint modulo 256 bytes.
+constexpr bool windows_disjoint(int stride, int rows, int bytes) {
+  for (int a = 1; a < rows; ++a) {
+    const int d = (a * stride) % 256;  // distance between rows r and r + a
+    if (d < bytes || 256 - d < bytes) return false;
+  }
+  return true;
+}
+
 template <int D>
 struct BGeo {
   static constexpr int NCH = D / 16;       // 16-wide k chunks of the head dim
   static constexpr int NDB = D / 32;       // 32-row blocks of a transposed accumulator
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
-  static constexpr int RS = D * 2 + 16;    // row stride, row-read copy
-  static constexpr int CS = D * 2 + 64;    // row stride, transposing-read copy
-  static constexpr int RT = kTile * RS;
-  static constexpr int CT = kTile * CS;
+  // Row stride of a staged tile: the smallest padding of whole 16-byte chunks that
+  // serves both read patterns (272 bytes at D = 128 would suit the row reads only).
+  static constexpr int SS = D == 128 ? 304 : 144;
+  static constexpr int ST = kTile * SS;    // bytes of one staged tile
+  static_assert(windows_disjoint(SS, 16, 16) && windows_disjoint(SS, 4, 32),
+                "the padded rows must keep both read patterns free of bank conflicts");
 };
 
 // Per-lane offsets of the two fragment read patterns (see the forward kernel):
 // row reads: row swap23(l32) of a 32-row block, chunk 2c + half at +32 c bytes;
 // transposing reads: rows 8 half + (lane & 15) / 4, head dims 16 ((lane >> 4) & 1) +
-// 4 (lane & 3); block (cc, db) at +16 cc CS + 64 db, high half at +4 CS.
-__device__ __forceinline__ int row_off(int lane, int RS) {
-  return swap23(lane & 31) * RS + (lane >> 5) * 16;
+// 4 (lane & 3); block (cc, db) at +16 cc SS + 64 db, high half at +4 SS (SS: the row stride).
+__device__ __forceinline__ int row_off(int lane, int SS) {
+  return swap23(lane & 31) * SS + (lane >> 5) * 16;
 }
-__device__ __forceinline__ int tr_off(int lane, int CS) {
-  return (8 * (lane >> 5) + ((lane & 15) >> 2)) * CS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+__device__ __forceinline__ int tr_off(int lane, int SS) {
+  return (8 * (lane >> 5) + ((lane & 15) >> 2)) * SS + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 }
 
 // A operand of rows [32 block] (row reads), k chunk c2.
@@ -90,10 +103,10 @@ __device__ __forceinline__ bf16x8_t frag_row(const uint8_t* base, int c2) {
   return as_bf16x8(load16(base + 32 * c2));
 }
 // A operand of the transposed block (head dims 32 db.., rows 16 cc + 8 half + 0..7).
-__device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* base, int cc, int db, int CS) {
-  const uint8_t* a0 = base + 16 * cc * CS + 64 * db;
+__device__ __forceinline__ bf16x8_t frag_tr(const uint8_t* base, int cc, int db, int SS) {
+  const uint8_t* a0 = base + 16 * cc * SS + 64 * db;
   const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0));
-  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0 + 4 * CS));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(v4i16_t, a0 + 4 * SS));
   const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
   return as_bf16x8(u32x4_t{l2[0], l2[1], h2[0], h2[1]});
 }
@@ -101,7 +114,7 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Direct global -> LDS staging of one 64-row tile (global_load_lds_dwordx4, as in the
+// Direct global -> LDS staging of 64-row tiles (global_load_lds_dwordx4, as in the
 // forward kernel) into a padded layout of C kilobytes (row stride 16 C bytes): one load
 // moves 64 lanes x 16 bytes to 1 KB of consecutive LDS at M0 + 16 lane, so lane i of
 // kilobyte j fills chunk 64 j + i of the padded tile, i.e. row (64 j + i) / C and column
@@ -111,33 +124,48 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // compiler, which does not see them write LDS, adds no waits before later LDS reads;
 // callers wait for them (vmcnt) before the barrier that publishes the tile. The
 // compiler makes no use of M0 in these kernels, which the assembly sets per load.
+// The source offsets depend only on the lane, the wavefront and (for the ragged last
+// tile) on N, so one set serves every tensor staged into the same layout.
 template <int D, int C, int WAVES>
-__device__ __forceinline__ void dma_tile(const uint16_t* src, const uint8_t* region, int t,
-                                         int N, int wave, int lane) {
-  constexpr int CPR = D / 8, MAXI = (C + WAVES - 1) / WAVES;
-  constexpr int kRowShift = __builtin_ctz(2 * D);
-  const uint64_t b64 = reinterpret_cast<uint64_t>(src) + uint64_t(t) * kTile * D * 2;
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(
-      uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64))))) |
-      (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
-  const bool ragged = t * kTile + kTile > N;
-  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(const uint8_t, region)));
-  const int ln = lane;
+struct Staging {
+  static constexpr int MAXI = (C + WAVES - 1) / WAVES;  // loads per wavefront and tile
+  uint32_t off[MAXI];  // byte offset of each load's source chunk within the tile
+
+  __device__ __forceinline__ Staging(int t, int N, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int kRowShift = __builtin_ctz(2 * D);
+    __builtin_assume(wave >= 0 && wave < WAVES);
+    // Last row of tile t that exists (>= kTile - 1 unless t is the ragged last tile).
+    const uint32_t last = uint32_t(N - 1 - t * kTile);
 #pragma unroll
-  for (int i = 0; i < MAXI; ++i) {
-    const int j = wave + WAVES * i;
-    if (j < C) {
-      const int p = 64 * j + ln, r = p / C, col = min(p % C, CPR - 1);
-      const int row = ragged ? min(t * kTile + r, N - 1) - t * kTile : r;
-      const uint32_t off = uint32_t(row << kRowShift) + uint32_t(col * 16);
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                   :
-                   : "s"(m0), "v"(off), "s"(base)
-                   : "memory");
+    for (int i = 0; i < MAXI; ++i) {
+      const uint32_t p = 64u * uint32_t(wave + WAVES * i) + uint32_t(lane);
+      const uint32_t r = p / C, col = min(p - r * C, uint32_t(CPR - 1));
+      off[i] = (min(r, last) << kRowShift) + col * 16u;
     }
   }
-}
+
+  __device__ __forceinline__ void issue(const uint16_t* src, const uint8_t* region, int t,
+                                        int wave) const {
+    __builtin_assume(wave >= 0 && wave < WAVES);
+    const uint64_t b64 = reinterpret_cast<uint64_t>(src) + uint64_t(t) * kTile * D * 2;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(
+        uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64))))) |
+        (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(b64 >> 32))))) << 32));
+    const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>(FA_LDS(const uint8_t, region)));
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int j = wave + WAVES * i;
+      if (j < C) {
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 1024u * uint32_t(j));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(m0), "v"(off[i]), "s"(base)
+                     : "memory");
+      }
+    }
+  }
+};
 // The lane index as the staging calls of one tile see it. At D = 128 it passes through
 // an empty asm statement once per tile, so the per-lane staging offsets are recomputed
 // for each tile (a few instructions, shared by the tile's calls of one layout) rather
@@ -176,7 +204,7 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
     const float* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ DELTA,
     float* __restrict__ dQ, int N, int BH, int nqt, float c, float scale) {
   using G = BGeo<D>;
-  constexpr int SLOT = 2 * G::RT + G::CT;  // K rows, K transposing copy, V rows
+  constexpr int SLOT = 2 * G::ST;  // K, then V
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -242,26 +270,24 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) ndl[r] = kFoldDelta ? -dl : 0.f;
 
-  // Staging: chunk i of a thread is row (tid + 256 i) / CPR, column (tid + 256 i) % CPR
-  // of the 64-key tile; rows past the end read the last row (finite; masked below).
-  // K (into its row and transposing layouts) and V (row layout) by direct loads.
-  constexpr int CR = G::RS / 16, CC = G::CS / 16;
-  static_assert(G::RT == CR * 1024 && G::CT == CC * 1024, "a padded tile is C kilobytes");
+  // Staging: K and V tiles of 64 keys by direct loads; rows past the end read the last
+  // row (finite; masked below).
+  constexpr int CS = G::SS / 16;
+  static_assert(G::ST == CS * 1024, "a padded tile is CS kilobytes");
   auto gload = [&](int t, int slot) __attribute__((always_inline)) {
     const uint8_t* s = smem + slot * SLOT;
-    const int sl = staging_lane<D>(lane);
-    dma_tile<D, CR, kWavesQ>(Kh, s, t, N, wave, sl);
-    dma_tile<D, CC, kWavesQ>(Kh, s + G::RT, t, N, wave, sl);
-    dma_tile<D, CR, kWavesQ>(Vh, s + G::RT + G::CT, t, N, wave, sl);
+    const Staging<D, CS, kWavesQ> st(t, N, wave, staging_lane<D>(lane));
+    st.issue(Kh, s, t, wave);
+    st.issue(Vh, s + G::ST, t, wave);
   };
-  const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
+  const int roff = row_off(lane, G::SS), toff = tr_off(lane, G::SS);
   const int first_masked = CAUSAL ? min(N >> 5, qw0 >> 5) : (N >> 5);
 
   auto step = [&](int g, const uint8_t* s) {
     const int b = (g & 1) * 32;
-    const uint8_t* kr = s + b * G::RS + roff;
-    const uint8_t* kt = s + G::RT + b * G::CS + toff;
-    const uint8_t* vr = s + G::RT + G::CT + b * G::RS + roff;
+    const uint8_t* kr = s + b * G::SS + roff;
+    const uint8_t* kt = s + b * G::SS + toff;
+    const uint8_t* vr = s + G::ST + b * G::SS + roff;
     f32x16_t st = f32x16_t{}, dp = ndl;
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) {
@@ -290,7 +316,7 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
       const u32x4_t bop = {ds[4 * cc], ds[4 * cc + 1], ds[4 * cc + 2], ds[4 * cc + 3]};
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
-        acc[db] = mfma(frag_tr(kt, cc, db, G::CS), as_bf16x8(bop), acc[db]);
+        acc[db] = mfma(frag_tr(kt, cc, db, G::SS), as_bf16x8(bop), acc[db]);
     }
   };
 
@@ -331,9 +357,8 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
     const float* __restrict__ LSE, const float* __restrict__ DELTA, float* __restrict__ dK,
     float* __restrict__ dV, int N, int BH, int nkt, float c, float scale) {
   using G = BGeo<D>;
-  // Q rows, Q transposing copy, dO rows, dO transposing copy, then lse2 and Delta of
-  // the tile's 64 queries.
-  constexpr int SLOT = 2 * G::RT + 2 * G::CT + 2 * kTile * 4;
+  // Q, dO, then lse2 and Delta of the tile's 64 queries.
+  constexpr int SLOT = 2 * G::ST + 2 * kTile * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -374,16 +399,14 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
 
   // Q and dO by direct loads, each into its row and transposing layouts; the 64 lse
   // and Delta values of a tile go through registers (threads 0..63).
-  constexpr int CR = G::RS / 16, CC = G::CS / 16;
-  static_assert(G::RT == CR * 1024 && G::CT == CC * 1024, "a padded tile is C kilobytes");
+  constexpr int CS = G::SS / 16;
+  static_assert(G::ST == CS * 1024, "a padded tile is CS kilobytes");
   float sl = 0.f, sdl = 0.f;
   auto gload = [&](int t, int slot) __attribute__((always_inline)) {
     const uint8_t* s = smem + slot * SLOT;
-    const int stl = staging_lane<D>(lane);
-    dma_tile<D, CR, kWavesB>(Qh, s, t, N, wave, stl);
-    dma_tile<D, CC, kWavesB>(Qh, s + G::RT, t, N, wave, stl);
-    dma_tile<D, CR, kWavesB>(dOh, s + G::RT + G::CT, t, N, wave, stl);
-    dma_tile<D, CC, kWavesB>(dOh, s + 2 * G::RT + G::CT, t, N, wave, stl);
+    const Staging<D, CS, kWavesB> st(t, N, wave, staging_lane<D>(lane));
+    st.issue(Qh, s, t, wave);
+    st.issue(dOh, s + G::ST, t, wave);
     if (tid < kTile) {
       const int q = t * kTile + tid;
       const float l = q < N ? lseh[q] : kNegInf;
@@ -394,12 +417,12 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   auto lstore = [&](int slot) __attribute__((always_inline)) {
     uint8_t* s = smem + slot * SLOT;
     if (tid < kTile) {
-      float* f = reinterpret_cast<float*>(s + 2 * G::RT + 2 * G::CT);
+      float* f = reinterpret_cast<float*>(s + 2 * G::ST);
       f[tid] = sl;
       f[kTile + tid] = sdl;
     }
   };
-  const int roff = row_off(lane, G::RS), toff = tr_off(lane, G::CS);
+  const int roff = row_off(lane, G::SS), toff = tr_off(lane, G::SS);
 
   // Registers 8 cc + 4 h4 + k hold query 32 g + 16 cc + 8 half + 4 h4 + k: each group
   // of four reads its four lse (P) or Delta (dS) values just before use.
@@ -407,7 +430,7 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   // carry no mask arithmetic.
   auto ew_p = [&](int g, const uint8_t* s, const f32x16_t& st, auto masked, uint32_t (&pk)[8])
       __attribute__((always_inline)) {
-    const float* fl = reinterpret_cast<const float*>(s + 2 * G::RT + 2 * G::CT) + (g & 1) * 32;
+    const float* fl = reinterpret_cast<const float*>(s + 2 * G::ST) + (g & 1) * 32;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -433,7 +456,7 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   auto ew_ds = [&](int g, const uint8_t* s, const f32x16_t& dp, const uint32_t (&pk)[8],
                    uint32_t (&dsk)[8]) __attribute__((always_inline)) {
     const float* fd =
-        reinterpret_cast<const float*>(s + 2 * G::RT + 2 * G::CT) + kTile + (g & 1) * 32;
+        reinterpret_cast<const float*>(s + 2 * G::ST) + kTile + (g & 1) * 32;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -450,19 +473,19 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   // dV^T += dO^T P or dK^T += Q^T dS for block g (transposing reads of the tile).
   auto tr_product = [&](int g, const uint8_t* tb0, const uint32_t (&b)[8], f32x16_t (&acc)[G::NDB])
       __attribute__((always_inline)) {
-    const uint8_t* tb = tb0 + (g & 1) * 32 * G::CS + toff;
+    const uint8_t* tb = tb0 + (g & 1) * 32 * G::SS + toff;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const u32x4_t bop = {b[4 * cc], b[4 * cc + 1], b[4 * cc + 2], b[4 * cc + 3]};
 #pragma unroll
       for (int db = 0; db < G::NDB; ++db)
-        acc[db] = mfma(frag_tr(tb, cc, db, G::CS), as_bf16x8(bop), acc[db]);
+        acc[db] = mfma(frag_tr(tb, cc, db, G::SS), as_bf16x8(bop), acc[db]);
     }
   };
   // S = Q K^T or dP = dO V^T of block g (row reads of the tile, own fragments).
   auto rows_product = [&](int g, const uint8_t* rb0, const u32x4_t (&own)[G::NCH], f32x16_t& out)
       __attribute__((always_inline)) {
-    const uint8_t* r = rb0 + (g & 1) * 32 * G::RS + roff;
+    const uint8_t* r = rb0 + (g & 1) * 32 * G::SS + roff;
     out = f32x16_t{};
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) out = mfma(frag_row(r, c2), as_bf16x8(own[c2]), out);
@@ -481,13 +504,13 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
       else
         ew_p(g, s, st, std::false_type{}, pk);
     }
-    tr_product(g, s + 2 * G::RT + G::CT, pk, dva);
+    tr_product(g, s + G::ST, pk, dva);
     {
       f32x16_t dp;
-      rows_product(g, s + G::RT + G::CT, vf, dp);
+      rows_product(g, s + G::ST, vf, dp);
       ew_ds(g, s, dp, pk, dsk);
     }
-    tr_product(g, s + G::RT, dsk, dka);
+    tr_product(g, s, dsk, dka);
   };
 
   const int ntiles = k0 >= N ? 0 : ntiles_all - t_first;
