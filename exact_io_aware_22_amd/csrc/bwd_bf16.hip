@@ -22,7 +22,8 @@
 //     and walks the query tiles, each 32-query block as one chain: S = Q K^T (A
 //     operand: Q rows from LDS), P element-wise (16 queries per lane, their lse read
 //     from LDS), dV^T += dO^T P (dO^T by the transposing LDS read); then dP = dO V^T,
-//     dS = P (dP - Delta) from the bf16 P the dV product used, dK^T += Q^T dS.
+//     dS = P (dP - Delta) from the bf16 P the dV product used (the dP products start
+//     from -Delta, so they yield dP - Delta), dK^T += Q^T dS.
 // Every product is v_mfma_f32_32x32x16_bf16; the element-wise results a lane holds
 // are, after bf16 packing, exactly the B operand of the next product (the swap23 row
 // order used by the forward kernel). A tile is read both row-wise (16-byte reads) and
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
     if (tid < kTile) {
       float* f = reinterpret_cast<float*>(s + 2 * G::ST);
       f[tid] = sl;
-      f[kTile + tid] = sdl;
+      f[kTile + tid] = -sdl;  // -Delta: the dP products accumulate onto it
     }
   };
   const int roff = row_off(lane, G::SS), toff = tr_off(lane, G::SS);
@@ -451,24 +452,28 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
         }
       }
   };
-  // dS = P (dP - Delta) of block g from the packed P (the values the dV product used);
-  // masked entries have P = 0, so dS needs no mask.
-  auto ew_ds = [&](int g, const uint8_t* s, const f32x16_t& dp, const uint32_t (&pk)[8],
-                   uint32_t (&dsk)[8]) __attribute__((always_inline)) {
-    const float* fd =
-        reinterpret_cast<const float*>(s + 2 * G::ST) + kTile + (g & 1) * 32;
+  // -Delta of block g's queries in accumulator order: the initial value of its dP
+  // products, which thereby yield dP - Delta.
+  auto neg_delta = [&](int g, const uint8_t* s) __attribute__((always_inline)) {
+    const float* fd = reinterpret_cast<const float*>(s + 2 * G::ST) + kTile + (g & 1) * 32;
+    f32x16_t init;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int h4 = 0; h4 < 2; ++h4) {
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(fd + 16 * cc + 8 * half + 4 * h4);
 #pragma unroll
-        for (int k2 = 0; k2 < 4; k2 += 2) {
-          const int r = 8 * cc + 4 * h4 + k2, i = r >> 1;
-          dsk[i] = pack_bf16x2(bf16_lo(pk[i]) * (dp[r] - d4[k2]),
-                               bf16_hi(pk[i]) * (dp[r + 1] - d4[k2 + 1]));
-        }
+        for (int k = 0; k < 4; ++k) init[8 * cc + 4 * h4 + k] = d4[k];
       }
+    return init;
+  };
+  // dS = P (dP - Delta) of block g from the packed P (the values the dV product used);
+  // masked entries have P = 0, so dS needs no mask.
+  auto ew_ds = [&](const f32x16_t& dpd, const uint32_t (&pk)[8], uint32_t (&dsk)[8])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dsk[i] = pack_bf16x2(bf16_lo(pk[i]) * dpd[2 * i], bf16_hi(pk[i]) * dpd[2 * i + 1]);
   };
   // dV^T += dO^T P or dK^T += Q^T dS for block g (transposing reads of the tile).
   auto tr_product = [&](int g, const uint8_t* tb0, const uint32_t (&b)[8], f32x16_t (&acc)[G::NDB])
@@ -482,11 +487,11 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
         acc[db] = mfma(frag_tr(tb, cc, db, G::SS), as_bf16x8(bop), acc[db]);
     }
   };
-  // S = Q K^T or dP = dO V^T of block g (row reads of the tile, own fragments).
+  // S = Q K^T or dP = dO V^T of block g (row reads of the tile, own fragments), added
+  // to the initial value of `out`.
   auto rows_product = [&](int g, const uint8_t* rb0, const u32x4_t (&own)[G::NCH], f32x16_t& out)
       __attribute__((always_inline)) {
     const uint8_t* r = rb0 + (g & 1) * 32 * G::SS + roff;
-    out = f32x16_t{};
 #pragma unroll
     for (int c2 = 0; c2 < G::NCH; ++c2) out = mfma(frag_row(r, c2), as_bf16x8(own[c2]), out);
   };
@@ -497,7 +502,7 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   auto step = [&](int g, const uint8_t* s) __attribute__((always_inline)) {
     uint32_t pk[8], dsk[8];
     {
-      f32x16_t st;
+      f32x16_t st = f32x16_t{};
       rows_product(g, s, kf, st);
       if ((32 * g + 32 > N) || (CAUSAL && 32 * g < kw0 + 32))
         ew_p(g, s, st, std::true_type{}, pk);
@@ -506,9 +511,9 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
     }
     tr_product(g, s + G::ST, pk, dva);
     {
-      f32x16_t dp;
+      f32x16_t dp = neg_delta(g, s);
       rows_product(g, s + G::ST, vf, dp);
-      ew_ds(g, s, dp, pk, dsk);
+      ew_ds(dp, pk, dsk);
     }
     tr_product(g, s, dsk, dka);
   };

@@ -40,8 +40,9 @@
 //   * K and V arrive 64 keys per tile through three-slot LDS rings by direct global ->
 //     LDS loads (global_load_lds_dwordx4, no register staging), issued two steps
 //     before the one barrier per tile that publishes them. Both are row-major in LDS with
-//     padded rows (K: +16 bytes, V: +64 bytes), which keeps the fragment reads free
-//     of bank conflicts on 64 LDS banks; slot offsets are uniform scalars rotated
+//     rows padded to one stride (304 bytes at D = 128, 144 at D = 64) that keeps both
+//     fragment read patterns free of bank conflicts on 64 LDS banks, so the two
+//     tensors share their staging offsets; slot offsets are uniform scalars rotated
 //     once per tile, so every fragment address is one per-lane base plus a constant.
 //   * Tiles where nothing is masked, ragged or final run in a loop of their own with
 //     no branches but the rare rescale; the remaining tiles take the general body,
@@ -90,8 +91,13 @@ struct Geo {
   static constexpr int NCH = D / 16;             // 16-wide k chunks of the head dim
   static constexpr int NDB = D / 32;             // 32-row blocks of O^T
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
-  static constexpr int KSTRIDE = D * 2 + 16;     // bytes per K row in LDS
-  static constexpr int VSTRIDE = D * 2 + 64;     // bytes per V row in LDS
+  // Bytes per K and V row in LDS. The K fragments are 16-byte row reads (16 lanes: 16
+  // rows at one column), the V fragments transposing reads (16 lanes: 4 rows x 32
+  // bytes); on 64 banks of 4 bytes, served 16 lanes at a time, both are conflict-free
+  // when those windows, spaced by the row stride, are disjoint modulo 256 bytes. One
+  // stride that satisfies both lets K and V share their staging offsets.
+  static constexpr int KSTRIDE = D == 128 ? 304 : 144;
+  static constexpr int VSTRIDE = KSTRIDE;
   static constexpr int KTILE = kBN * KSTRIDE;
   static constexpr int VTILE = kBN * VSTRIDE;
   static constexpr int LDS = kSlots * (KTILE + VTILE);
@@ -198,12 +204,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int p = 64 * j + lane, r = p / C, col = min(p % C, G::CPR - 1);
     return uint32_t(r * D * 2 + col * 16);
   };
-  uint32_t dk[MAXI], dv[MAXI];
+  static_assert(CK == CV, "K and V tiles share one layout, hence one set of offsets");
+  uint32_t dk[MAXI];
 #pragma unroll
-  for (int i = 0; i < MAXI; ++i) {
-    dk[i] = chunk_off(wave + kWaves * i, CK);
-    dv[i] = chunk_off(wave + kWaves * i, CV);
-  }
+  for (int i = 0; i < MAXI; ++i) dk[i] = chunk_off(wave + kWaves * i, CK);
+  const uint32_t (&dv)[MAXI] = dk;
   // The same chunk in tile t when rows past N - 1 are redirected to row N - 1 (its row
   // is off / (2D), a power-of-two division).
   auto clamp_off = [&](uint32_t off, int t) __attribute__((always_inline)) -> uint32_t {
