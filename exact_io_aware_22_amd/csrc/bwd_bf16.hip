@@ -131,7 +131,12 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // callers wait for them (vmcnt) before the barrier that publishes the tile. The
 // compiler makes no use of M0 in these kernels, which the assembly sets per load.
 // The source offsets depend only on the lane, the wavefront and (for the ragged last
-// tile) on N, so one set serves every tensor staged into the same layout.
+// tile) on N, so one set serves every tensor staged into the same layout; the compiler
+// keeps each load's row and chunk in registers across the tile loop and forms the
+// offsets with two instructions per load. (With two layouts, twice the offsets kept
+// that way pushed the dK/dV kernel past 256 registers, and a spilled offset reloaded
+// between two staging loads waited for every load in flight; they were recomputed at
+// every tile instead.)
 template <int D, int C, int WAVES>
 struct Staging {
   static constexpr int MAXI = (C + WAVES - 1) / WAVES;  // loads per wavefront and tile
@@ -172,17 +177,6 @@ struct Staging {
     }
   }
 };
-// The lane index as the staging calls of one tile see it. At D = 128 it passes through
-// an empty asm statement once per tile, so the per-lane staging offsets are recomputed
-// for each tile (a few instructions, shared by the tile's calls of one layout) rather
-// than kept across the tile loop in registers the products need: kept, they pushed the
-// dK/dV kernel past 256 registers, and a spilled offset reloaded between two staging
-// loads waited for every load in flight.
-template <int D>
-__device__ __forceinline__ int staging_lane(int lane) {
-  if constexpr (D == 128) asm volatile("" : "+v"(lane));
-  return lane;
-}
 // s_waitcnt vmcnt(0), through the builtin so the compiler's own bookkeeping sees it.
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -282,7 +276,7 @@ __global__ __launch_bounds__(kThreadsQ, 1) void dq_kernel(
   static_assert(G::ST == CS * 1024, "a padded tile is CS kilobytes");
   auto gload = [&](int t, int slot) __attribute__((always_inline)) {
     const uint8_t* s = smem + slot * SLOT;
-    const Staging<D, CS, kWavesQ> st(t, N, wave, staging_lane<D>(lane));
+    const Staging<D, CS, kWavesQ> st(t, N, wave, lane);
     st.issue(Kh, s, t, wave);
     st.issue(Vh, s + G::ST, t, wave);
   };
@@ -410,7 +404,7 @@ __global__ __launch_bounds__(KV<D>::kThreads, 1) void dkdv_kernel(
   float sl = 0.f, sdl = 0.f;
   auto gload = [&](int t, int slot) __attribute__((always_inline)) {
     const uint8_t* s = smem + slot * SLOT;
-    const Staging<D, CS, kWavesB> st(t, N, wave, staging_lane<D>(lane));
+    const Staging<D, CS, kWavesB> st(t, N, wave, lane);
     st.issue(Qh, s, t, wave);
     st.issue(dOh, s + G::ST, t, wave);
     if (tid < kTile) {
