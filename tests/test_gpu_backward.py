@@ -73,6 +73,21 @@ def test_backward_sizes(dtype, D, causal, N):
     check(got, ref, dtype, f"N={N} D={D} causal={causal}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("N", [1537, 2049])
+def test_backward_sizes_past_1024(D, causal, N):
+    """Several 256-row query and key tiles of the two kernels, each length one row past a
+    64-row staging tile (the ragged last tile stages row N - 1 into its missing rows)."""
+    seed = 7000 + N + 7 * D + (1 if causal else 0)
+    q, k, v, do = (random_tensor((1, 2, N, D), seed + i, torch.bfloat16) for i in range(4))
+    scale = 1 / math.sqrt(D)
+    say(f"backward N={N} D={D} causal={causal} bf16")
+    got = run_backward(q, k, v, do, scale, causal)
+    ref = oracle.attention_backward(q, k, v, do, scale, causal)[:3]
+    check(got, ref, torch.bfloat16, f"N={N} D={D} causal={causal}")
+
+
 def test_backward_large_scores_and_batches():
     """Several heads and batches, scores in the tens (q, k ~ N(0, 9))."""
     q, k = (random_tensor((2, 3, 300, 128), 40 + i, torch.bfloat16, sigma=3.0) for i in range(2))

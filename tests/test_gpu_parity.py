@@ -133,10 +133,10 @@ def test_full_size_prefill_all_rows(name):
 # ------------------------------------------------------------------ sizes past one tile row
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-@pytest.mark.parametrize("N", [2049, 4095, 4097])
-def test_forward_sizes_beyond_2048(D, causal, N):
+@pytest.mark.parametrize("N", [1031, 1537, 2049, 4095, 4097])
+def test_forward_sizes_past_1024(D, causal, N):
     """Lengths just past and just short of whole 256-row query tiles and 64-key tiles,
-    bf16, every row compared."""
+    between 1024 and 2048 as well as past 2048, bf16, every row compared."""
     seed = 5000 + 3 * N + D + int(causal)
     q, k, v = (random_tensor((1, 2, N, D), seed + i, torch.bfloat16) for i in range(3))
     scale = 1.0 / math.sqrt(D)
