@@ -46,3 +46,40 @@ def test_m0_is_only_the_staging_loads_destination(src):
         if l.startswith("global_load_lds_dwordx4"):
             loads += 1
     assert writes > 0 and writes == loads, (writes, loads)
+
+
+def kernel_resources(asm: str):
+    """(name, vgprs, agprs, scratch bytes per lane, LDS bytes) of every kernel, from the
+    code object metadata the compiler emits with the assembly."""
+    out = []
+    for block in re.split(r"\n\s*- \.", asm.split("amdhsa.kernels:")[-1])[1:]:
+        def field(key):
+            m = re.search(rf"\.?{key}:\s+(\S+)", block)
+            return m.group(1) if m else None
+        name = field("name")
+        if name is None or field("vgpr_count") is None:
+            continue
+        out.append((name, int(field("vgpr_count")), int(field("agpr_count") or 0),
+                    int(field("private_segment_fixed_size")),
+                    int(field("group_segment_fixed_size"))))
+    return out
+
+
+@pytest.mark.parametrize("src,kernels", [
+    ("fwd_bf16.hip", ["fwd_bf16_kernel"]),
+    ("bwd_bf16.hip", ["dq_kernel", "dkdv_kernel"]),
+    ("decode.hip", ["decode_partials_kernel", "decode_partials_wave_kernel", "combine_kernel"]),
+    ("reduce.hip", ["row_reduce_kernel", "row_scan_kernel"]),
+])
+def test_hot_kernels_keep_their_occupancy_without_scratch(src, kernels):
+    """Every instance of the hot kernels compiles without scratch (no spilled registers,
+    no private arrays) and within 256 VGPRs, so two wavefronts fit each SIMD; the
+    MFMA kernels use 160 KB of LDS or less, one workgroup per CU."""
+    res = kernel_resources(device_asm(src))
+    for k in kernels:
+        mine = [r for r in res if k + "I" in r[0]]
+        assert mine, f"{src}: no instance of {k} in {[r[0] for r in res]}"
+        for name, vgpr, agpr, scratch, lds in mine:
+            assert scratch == 0, f"{name}: {scratch} bytes of scratch per lane"
+            assert vgpr + agpr <= 256, f"{name}: {vgpr} VGPRs + {agpr} AGPRs"
+            assert lds <= 160 * 1024, f"{name}: {lds} bytes of LDS"
