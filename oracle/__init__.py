@@ -17,7 +17,11 @@ from .fp64 import (  # noqa: F401
     safe_softmax_rows,
     split_bounds,
 )
-from .backward import attention_backward  # noqa: F401,E402
+from .backward import (  # noqa: F401,E402
+    attention_backward,
+    attention_backward_dq_rows,
+    attention_backward_row_block,
+)
 from .masks import attention_varlen, attention_window, visible  # noqa: F401,E402
 from .monoids import (  # noqa: F401,E402
     log_sum_exp,

@@ -97,3 +97,37 @@ def attention_backward(q, k, v, do, scale: float, causal: bool = False, row_bloc
         for bh in heads:
             run(bh)
     return dq, dk, dv, delta
+
+
+def attention_backward_dq_rows(q, k, v, do, scale: float, causal: bool, rows):
+    """dQ for a chosen set of query rows only: rows is an iterable of (b, h, i).
+
+    Row i of dQ = scale dS_i K needs only row i of Q and dO and all of K and V (P_i,
+    dP_i and Delta_i are all row-local), so each row is computed alone by the same
+    row-block routine as attention_backward, with a block of one row. Returns float64
+    [len(rows), D].
+    """
+    rows = list(rows)
+    out = np.zeros((len(rows), q.shape[3]), dtype=np.float64)
+    head = None
+    for n, (b, h, i) in enumerate(rows):
+        if head is None or head[0] != (b, h):
+            head = ((b, h), _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h]))
+        _, qh, kh, vh, doh = head
+        gq, _, _, _ = _backward_rows(qh, kh, vh, doh, float(scale), causal, i, i + 1)
+        out[n] = gq[0]
+    return out
+
+
+def attention_backward_row_block(q, k, v, do, scale: float, causal: bool, b: int, h: int,
+                                 r0: int, r1: int):
+    """The gradient contributions of query rows [r0, r1) of head (b, h): dQ of those
+    rows [r1-r0, D] and their parts of dK [Nk, D] and dV [Nk, Dv] (float64).
+
+    Under the causal mask key j is seen only by queries i >= j, so for r1 = N the parts
+    are the whole dK and dV of keys j >= r0: the last keys' gradients need only the last
+    query rows.
+    """
+    gq, gk, gv, _ = _backward_rows(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]),
+                                   _f64(do[b, h]), float(scale), causal, r0, r1)
+    return gq, gk, gv

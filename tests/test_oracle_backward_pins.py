@@ -182,3 +182,29 @@ def test_matches_torch_autograd_float64(causal):
     np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_match_the_full_backward(causal):
+    """The row-sampled dQ (used at sizes the full oracle cannot hold) is the full
+    backward's dQ on those rows: the same routine, one row at a time."""
+    g = torch.Generator().manual_seed(321)
+    q, k, v, do = (torch.randn(2, 2, 37, 16, generator=g, dtype=torch.float64) for _ in range(4))
+    dq = oracle.attention_backward(q, k, v, do, 0.3, causal)[0]
+    rows = [(0, 0, 0), (0, 1, 36), (1, 0, 17), (1, 1, 5), (1, 1, 36)]
+    got = oracle.attention_backward_dq_rows(q, k, v, do, 0.3, causal, rows)
+    want = np.stack([dq[b, h, i] for b, h, i in rows])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_causal_tail_block_gives_the_last_keys_whole_gradients():
+    """Under the causal mask the last r keys are seen only by the last r queries, so the
+    row block [N - r, N) alone gives their complete dK and dV (as in the full backward)."""
+    g = torch.Generator().manual_seed(654)
+    q, k, v, do = (torch.randn(1, 2, 40, 8, generator=g, dtype=torch.float64) for _ in range(4))
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.5, True)
+    gq, gk, gv = oracle.attention_backward_row_block(q, k, v, do, 0.5, True, 0, 1, 28, 40)
+    np.testing.assert_allclose(gq, dq[0, 1, 28:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gk[28:], dk[0, 1, 28:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gv[28:], dv[0, 1, 28:], rtol=1e-12, atol=1e-14)
+    assert np.max(np.abs(gk[:28] - dk[0, 1, :28])) > 1e-3  # earlier keys need earlier rows
