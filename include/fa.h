@@ -76,6 +76,12 @@ enum {
  *   D       : head dimension, 64 or 128.
  * Scores are formed from the inputs exactly as given, accumulated in float32; the
  * probabilities fed to the P V product are rounded to the input type.
+ * Range: each weight's exponent is formed as s c - m c in one float32 fused
+ * multiply-add (c = scale log2 e, m the running maximum), so the rounding of m c,
+ * |m c| 2^-24, enters it. Results hold to bf16 precision while the scaled scores stay
+ * below about 2e4 in magnitude (attention's are tens to hundreds); far larger ones
+ * (a scale of 1e20 on unit-size inputs) lose the weights and can come back as NaN.
+ * The same holds for fa_forward_ext, fa_decode_partials and fa_backward.
  */
 int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                int B, int H, int N, int D, float scale, int causal, int dtype,

@@ -157,6 +157,45 @@ def _overflowing_fp32_inputs(shape_q, shape_kv, seed):
     return q, k, v
 
 
+@pytest.mark.parametrize("scale", [1e-30, 400.0], ids=["tiny", "large"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_forward_extreme_scales(scale, D, causal):
+    """The two ends of the softmax. A scale of 1e-30 makes every visible key weigh the
+    same (O = mean of the visible values, lse = ln of their count). A scale of 400 puts
+    the scaled scores near 2e4, where the largest score takes all the weight and every
+    step whose block holds a new maximum goes through the rare path; that is about the
+    largest magnitude the kernels' exponents (s c - m c in one fused multiply-add, c =
+    scale log2 e) keep to bf16 precision, |m c| <= 2^15. lse is compared relative to its
+    size there (float32 spacing at 2e4 is 2e-3)."""
+    seed = 6100 + D + int(causal) + (7 if scale > 1 else 0)
+    q, k, v = (random_tensor((1, 2, 300, D), seed + i, torch.bfloat16) for i in range(3))
+    say(f"forward scale={scale:g} D={D} causal={causal}")
+    o, lse = run_forward(q, k, v, scale, causal)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    err_o = float(np.max(np.abs(o - o_ref)))
+    err_l = float(np.max(np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))))
+    say(f"max|dO|={err_o:.3e} max|dlse|/max(1,|lse|)={err_l:.3e} max|lse|={np.max(np.abs(lse_ref)):.3g}")
+    assert err_o <= TOL_O[torch.bfloat16]
+    assert err_l <= TOL_LSE * (1e-3 if scale > 1 else 1)
+
+
+@pytest.mark.parametrize("scale", [1e-30, 400.0], ids=["tiny", "large"])
+def test_decode_extreme_scales(scale):
+    """Split-KV decode at both ends of the softmax (see test_forward_extreme_scales)."""
+    q = random_tensor((1, 4, 1, 128), 6200, torch.bfloat16)
+    k, v = (random_tensor((1, 4, 3000, 128), 6201 + i, torch.bfloat16) for i in range(2))
+    _, _, _, o, lse = run_decode(q, k, v, scale, 16)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, False)
+    err_o = float(np.max(np.abs(o - o_ref.reshape(4, 128))))
+    lr = lse_ref.reshape(4)
+    err_l = float(np.max(np.abs(lse - lr) / np.maximum(1.0, np.abs(lr))))
+    say(f"decode scale={scale:g}: max|dO|={err_o:.3e} max|dlse|/max(1,|lse|)={err_l:.3e}")
+    assert err_o <= TOL_O[torch.bfloat16]
+    assert err_l <= TOL_LSE * (1e-3 if scale > 1 else 1)
+
+
 def test_fp32_unscaled_scores_overflow_exp():
     """Safe softmax in float32: scale = 1 puts raw scores above 88.72, so e^s overflows
     float32 without the maximum subtracted ("Softmax Looks Like It Breaks the Rules");
