@@ -95,13 +95,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partials_kernel(
       const float m_new = fmaxf(m_run, mx);
       const float mref = m_new == kNegInf ? 0.f : m_new;
       const float alpha = exp2_hw((m_run - mref) * c);
-      const float nmc = -mref * c;
       d_run *= alpha;
 #pragma unroll
       for (int e = 0; e < E; ++e) o[e] *= alpha;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const float p = exp2_hw(fmaf(s[i], c, nmc));
+        // The maximum is subtracted before scaling, so the largest weight is exactly 1
+        // at any magnitude of the scores (the stream is HBM-bound; the extra
+        // instruction costs nothing here).
+        const float p = exp2_hw((s[i] - mref) * c);
         d_run += p;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -216,14 +218,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partials_wave_kernel(
     }
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float nmc = -(mx == kNegInf ? 0.f : mx) * c;
+    const float mref = mx == kNegInf ? 0.f : mx;
     float den = 0.f;
     float o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.f;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const float p = exp2_hw(fmaf(s[i], c, nmc));
+      const float p = exp2_hw((s[i] - mref) * c);  // maximum subtracted before scaling
       den += p;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {

@@ -81,7 +81,8 @@ enum {
  * |m c| 2^-24, enters it. Results hold to bf16 precision while the scaled scores stay
  * below about 2e4 in magnitude (attention's are tens to hundreds); far larger ones
  * (a scale of 1e20 on unit-size inputs) lose the weights and can come back as NaN.
- * The same holds for fa_forward_ext, fa_decode_partials and fa_backward.
+ * The same holds for fa_forward_ext and fa_backward; fa_decode_partials subtracts
+ * the maximum before scaling and holds at any magnitude.
  */
 int fa_forward(const void* q, const void* k, const void* v, float* o, float* lse,
                int B, int H, int N, int D, float scale, int causal, int dtype,

@@ -181,9 +181,11 @@ def test_forward_extreme_scales(scale, D, causal):
     assert err_l <= TOL_LSE * (1e-3 if scale > 1 else 1)
 
 
-@pytest.mark.parametrize("scale", [1e-30, 400.0], ids=["tiny", "large"])
+@pytest.mark.parametrize("scale", [1e-30, 400.0, 1e20], ids=["tiny", "large", "huge"])
 def test_decode_extreme_scales(scale):
-    """Split-KV decode at both ends of the softmax (see test_forward_extreme_scales)."""
+    """Split-KV decode at both ends of the softmax (see test_forward_extreme_scales). The
+    decode subtracts each chunk's maximum before scaling, so it also holds at scaled
+    scores near 1e21 (a scale of 1e20)."""
     q = random_tensor((1, 4, 1, 128), 6200, torch.bfloat16)
     k, v = (random_tensor((1, 4, 3000, 128), 6201 + i, torch.bfloat16) for i in range(2))
     _, _, _, o, lse = run_decode(q, k, v, scale, 16)
