@@ -162,6 +162,44 @@ def test_varlen_max_seqlen_caps_sequences():
     assert np.all(np.isnan(o[:, 40 + cap:740])), "rows past max_seqlen written"
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_varlen_inconsistent_offsets_are_clamped(causal):
+    """Offsets are clamped on the device (a = clamp(cu[s], 0, N), b = clamp(cu[s+1], a,
+    N)), so decreasing, negative or oversized entries still define sequences inside the
+    tensors: nothing is read or written outside them (guard rows around o and lse stay
+    untouched) and each clamped sequence is attention on its own rows. With cu = [0, 120,
+    60, 250, 400] the sequences are [0, 120), [120, 120), [60, 250) and [250, 400): rows
+    60-119 belong to two sequences, whose stores may interleave: each of their elements
+    holds one of the two results."""
+    D, total, pad = 128, 400, 64
+    q, k, v = (random_tensor((1, total, D), 480 + i + 3 * int(causal), torch.bfloat16)
+               for i in range(3))
+    for cu, seqs in (([0, 120, 60, 250, 400], [(0, 120), (60, 250), (250, 400)]),
+                     ([-5, 100, 5000], [(0, 100), (100, total)])):
+        o_big = torch.full((1, pad + total + pad, D), float("nan"), device="cuda")
+        l_big = torch.full((1, pad + total + pad), float("nan"), device="cuda")
+        o, lse = o_big[:, pad:pad + total], l_big[:, pad:pad + total]
+        cud = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        fa.fa_forward_ext(q.cuda(), k.cuda(), v.cuda(), o, lse, 0.1, causal, -1, -1, cud, total)
+        torch.cuda.synchronize()
+        say(f"clamped offsets {cu} causal={causal}")
+        assert bool(torch.isnan(o_big[:, :pad]).all() and torch.isnan(o_big[:, pad + total:]).all())
+        assert bool(torch.isnan(l_big[:, :pad]).all() and torch.isnan(l_big[:, pad + total:]).all())
+        got_o, got_l = o.cpu().double().numpy()[0], lse.cpu().double().numpy()[0]
+        refs = {}
+        for a, b in seqs:
+            ro, rl = oracle.attention(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], 0.1, causal)
+            refs[(a, b)] = (ro[0, 0], rl[0, 0])
+        for i in range(total):
+            owners = [(a, b) for a, b in seqs if a <= i < b]
+            assert owners, i
+            # two sequences' stores of one row may interleave: every element must be
+            # one of its owners' values
+            d_o = np.min([np.abs(got_o[i] - refs[s][0][i - s[0]]) for s in owners], axis=0)
+            d_l = min(abs(got_l[i] - refs[s][1][i - s[0]]) for s in owners)
+            assert np.max(d_o) <= TOL_O and d_l <= TOL_LSE, f"row {i}, sequences {owners}"
+
+
 # ------------------------------------------------------------------ full size
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("window", [1024, 4096])
