@@ -557,8 +557,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build measures one MI355X; there is no "
-              "multi-GPU path to time (--gpus must be 1).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path to time "
+              "(--gpus must be 1).", file=sys.stderr)
         return 2
 
     import torch

@@ -11,7 +11,7 @@
 //     every launch configuration (1 <= grid <= 2^31 - 1 workgroups, one-dimensional,
 //     whole wavefronts of at most 1024 threads, dynamic LDS within 160 KiB) and records
 //     it; the fat binary registration is a no-op, so no device code is needed.
-// Either way the driver then
+// Either way the program then
 //   1. makes calls with known answers: the documented error codes, and what a valid
 //      call reaches;
 //   2. sweeps every entry point over extreme integer and float arguments (INT_MIN,
