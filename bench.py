@@ -37,7 +37,8 @@ DECODE = "split_kv_decode"
 MASKED = ["sliding_window_4096_causal_d128", "sliding_window_1024_causal_d128",
           "varlen_causal_d128"]
 EXTRA = ["batched_prefill_d64", "batched_prefill_d64_causal", "long_context_causal_32768",
-         "long_context_causal_32767"]
+         "long_context_causal_32767", "single_head_fp32"]
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector ALU
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": "exact_io_aware_22_amd/csrc/fwd_bf16.hip",
     "decode_partials_kernel": "exact_io_aware_22_amd/csrc/decode.hip",
@@ -205,7 +206,7 @@ def measured_ceilings(steps: int, warmup: int, torch, fa):
 
 
 def bench_prefill(name: str, steps: int, warmup: int, torch, fa, make_inputs, W,
-                  per_launch=False):
+                  per_launch=False, graph=False):
     w = W[name]
     q, k, v = make_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
@@ -216,6 +217,20 @@ def bench_prefill(name: str, steps: int, warmup: int, torch, fa, make_inputs, W,
     res = {"workload": name, "ms": ms, "tflops": w.flops() / (ms * 1e-3) / 1e12}
     if per_launch:
         res["per_launch"] = time_each(launch, max(20, steps), torch)
+    if graph:
+        # A launch shorter than the binding's host-side cost is timed back to back from a
+        # HIP graph of `reps` launches, so the GPU never waits for the host between them.
+        reps = 64
+        launch()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                launch()
+        ms_graph = time_launches(g.replay, max(10, steps // 4), 3, torch) / reps
+        res["graph"] = {"launches_per_replay": reps, "ms": ms_graph,
+                        "tflops": w.flops() / (ms_graph * 1e-3) / 1e12}
+        del g
     del qd, kd, vd, o, lse
     return res, (q, k, v)
 
@@ -592,23 +607,29 @@ def main() -> int:
         w = WORKLOADS[name]
         log(f"timing {name}")
         head, (q, k, v) = bench_prefill(name, args.steps, args.warmup, torch, fa, make_inputs,
-                                        WORKLOADS, per_launch=True)
-        ms = head["ms"]
+                                        WORKLOADS, per_launch=True,
+                                        graph=w.dtype == torch.float32)
+        # the float32 workload's launches are shorter than an eager call's host-side cost
+        ms = head["graph"]["ms"] if "graph" in head else head["ms"]
         flops = w.flops()
         achieved = flops / (ms * 1e-3) / 1e12
+        fp32 = w.dtype == torch.float32  # only when asked for with --workload
+        peak = PEAK_FP32_VECTOR_TFLOPS if fp32 else PEAK_BF16_TFLOPS
         out.update({
             "value": achieved, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "vs_baseline": None, "dtype": "f32" if fp32 else "bf16", "data": "synthetic",
             "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                        "causal": w.causal, "sigma_qk": w.sigma_qk, "parallelism": "single GPU"},
-            "roofline": {"kernel": "fwd_bf16_kernel", "bound": "mfma", "achieved": achieved,
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": achieved / PEAK_BF16_TFLOPS,
-                         "traffic": measured_traffic("fwd_bf16_kernel", name),
+            "roofline": {"kernel": "fwd_f32_kernel" if fp32 else "fwd_bf16_kernel",
+                         "bound": "alu" if fp32 else "mfma", "achieved": achieved,
+                         "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                         "traffic": None if fp32 else measured_traffic("fwd_bf16_kernel", name),
                          "algorithmic_flops_per_launch": flops},
         })
         out["per_launch"] = head["per_launch"]
+        if "graph" in head:
+            out["graph"] = head["graph"]
         if args.only == "all" and not args.no_cpu_baseline:
             log("timing the fp64 oracle on host cores")
             out["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_seconds)
@@ -617,9 +638,18 @@ def main() -> int:
             out["also"] = []
             for name in EXTRA:
                 log(f"timing {name}")
+                fp32 = WORKLOADS[name].dtype == torch.float32
                 r, _ = bench_prefill(name, max(3, args.steps // 2), max(1, args.warmup // 2), torch,
-                                     fa, make_inputs, WORKLOADS)
-                r["frac_of_bf16_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
+                                     fa, make_inputs, WORKLOADS, per_launch=fp32, graph=fp32)
+                if fp32:
+                    # float32 inputs take the vector-ALU kernels; at this size one launch is
+                    # a few microseconds, so its time, not a fraction, is the figure: the
+                    # kernel's from graph replay, and one eager call's through the binding
+                    r["us"] = r["graph"]["ms"] * 1e3
+                    r["us_eager_call"] = r["ms"] * 1e3
+                    r["frac_of_fp32_vector_peak"] = r["graph"]["tflops"] / PEAK_FP32_VECTOR_TFLOPS
+                else:
+                    r["frac_of_bf16_peak"] = r["tflops"] / PEAK_BF16_TFLOPS
                 out["also"].append(r)
                 torch.cuda.empty_cache()
     if args.only in ("all", "backward"):
