@@ -554,13 +554,54 @@ def copy_calibration(torch, nbytes: int, steps: int):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "steps": steps}))
 
 
+def sustain(seconds: float, torch, fa, make_inputs, W):
+    """Each kernel family launched back to back for `seconds` of wall time (after an idle
+    stretch of the same length), one JSON line per phase with its start and end times
+    (Unix seconds) and call count, for reading the board's power and clock sensors
+    (amd-smi, sampled by the caller) against the phases. Prints as it goes."""
+    def phase(name, fn):
+        t0 = time.time()
+        n = 0
+        while time.time() < t0 + seconds:
+            for _ in range(16):
+                fn()
+            torch.cuda.synchronize()
+            n += 16
+        print(json.dumps({"phase": name, "start": t0, "end": time.time(), "calls": n}), flush=True)
+
+    t0 = time.time()
+    time.sleep(seconds)
+    print(json.dumps({"phase": "idle", "start": t0, "end": time.time(), "calls": 0}), flush=True)
+    chk = torch.empty(1024 * 512, device="cuda")
+    phase("mfma_only_loop", lambda: fa.fa_calibrate_mfma(chk, 1024, 256, seed=1))
+    w = W[HEADLINE]
+    q, k, v = (t.cuda() for t in make_inputs(w))
+    o = torch.empty(w.B, w.H, w.N, w.D, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+    phase("forward_" + HEADLINE, lambda: fa.fa_forward(q, k, v, o, lse, w.scale, w.causal))
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed + 100)
+    do = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).cuda()
+    delta = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device="cuda")
+    grads = [torch.empty_like(o) for _ in range(3)]
+    phase("backward_" + HEADLINE,
+          lambda: fa.fa_backward(q, k, v, o, lse, do, delta, *grads, w.scale, w.causal))
+    del q, k, v, o, lse, do, delta, grads
+    torch.cuda.empty_cache()
+    wd = W[DECODE]
+    qd, kd, vd = (t.cuda() for t in make_inputs(wd))
+    od = torch.empty(wd.B * wd.H, wd.D, device="cuda")
+    ld = torch.empty(wd.B * wd.H, device="cuda")
+    phase("decode_" + DECODE, lambda: fa.fa_decode_noalloc(qd, kd, vd, od, ld, wd.scale, wd.splits))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "masks",
-                                       "reductions", "copy", "ceilings", "overlap"],
+                                       "reductions", "copy", "ceilings", "overlap", "sustain"],
                     default="all")
     ap.add_argument("--workload", default=HEADLINE, choices=[HEADLINE] + EXTRA,
                     help="with --only prefill: the prefill workload to time (default: the "
@@ -568,6 +609,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--seconds", type=float, default=10.0,
+                    help="with --only sustain: wall time of each phase")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -596,6 +639,9 @@ def main() -> int:
         return 0
     if args.only == "overlap":
         print(json.dumps({"overlap": measure_overlap(torch, fa)}))
+        return 0
+    if args.only == "sustain":
+        sustain(args.seconds, torch, fa, make_inputs, WORKLOADS)
         return 0
 
     out = {"metric": METRIC}
