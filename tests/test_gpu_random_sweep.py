@@ -257,3 +257,62 @@ def test_random_decode(c):
     assert float(err_op.max()) <= TOL_PART_O[dtype], f"{what}: partial o {err_op.max()}"
     o_ref, lse_ref = oracle.attention(q, k, v, c["scale"], False)
     _check_o(o, lse, o_ref.reshape(rows, D), lse_ref.reshape(rows), dtype, what)
+
+
+# ------------------------------------------------------------------ row reductions and scans
+# Random row counts, lengths, element offsets (rows on and off 16-byte boundaries),
+# dtypes and value ranges, some scores at -inf; the bounds are those of the reduction
+# and scan tests (tests/test_gpu_reductions.py, tests/test_gpu_scans.py), whose helpers
+# run and check the calls.
+from tests import test_gpu_reductions as _red  # noqa: E402
+from tests import test_gpu_scans as _scan  # noqa: E402
+
+
+def _row_cases(count, seed, max_n):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        cases.append(dict(i=i, rows=int(rng.integers(1, 41)), n=int(rng.integers(1, max_n)),
+                          dt=str(rng.choice(["bf16", "fp32"])), offset=int(rng.integers(0, 8)),
+                          sigma=float(rng.choice([0.5, 4.0, 30.0])),
+                          mean=float(rng.choice([0.0, 3.0, -100.0])),
+                          masked=float(rng.choice([0.0, 0.0, 0.3])),
+                          seed=int(rng.integers(1, 2**30))))
+    return cases
+
+
+def _row_input(c, masked_ok):
+    x = random_tensor((c["rows"], c["n"]), c["seed"], torch.float32, sigma=c["sigma"]) + c["mean"]
+    if masked_ok and c["masked"] > 0:
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(c["seed"] + 1)
+        x[torch.rand(x.shape, generator=gen) < c["masked"]] = float("-inf")
+    return x.to(DT[c["dt"]])
+
+
+REDUCE = _row_cases(16, 20261208, 40000)
+SCAN = _row_cases(16, 20261209, 9000)
+
+
+@pytest.mark.parametrize("c", REDUCE, ids=lambda c: f"r{c['rows']}n{c['n']}{c['dt']}o{c['offset']}")
+def test_random_row_reductions(c):
+    what = f"reductions {c}"
+    say(what)
+    x = _row_input(c, True)
+    m, d = _red.run(fa.fa_softmax_stats, x, c["offset"])
+    _red.check_softmax(x, m, d, "softmax_stats " + what)
+    x = _row_input(c, False)
+    mean, m2 = _red.run(fa.fa_moments, x, c["offset"])
+    _red.check_moments(x, mean, m2, "moments " + what)
+
+
+@pytest.mark.parametrize("c", SCAN, ids=lambda c: f"r{c['rows']}n{c['n']}{c['dt']}o{c['offset']}")
+def test_random_row_scans(c):
+    what = f"scans {c}"
+    say(what)
+    x = _row_input(c, True)
+    m, d = _scan.run(fa.fa_softmax_scan, x, c["offset"])
+    _scan.check_softmax_scan(x, m, d, "softmax_scan " + what)
+    x = _row_input(c, False)
+    mean, m2 = _scan.run(fa.fa_moments_scan, x, c["offset"])
+    _scan.check_moments_scan(x, mean, m2, "moments_scan " + what)
