@@ -526,20 +526,29 @@ def bench_reductions(steps: int, warmup: int, torch, fa):
         # float32 outputs per element)
         sa = torch.empty(w.rows, w.n, device="cuda")
         sb = torch.empty(w.rows, w.n, device="cuda")
-        sfn = fa.fa_softmax_scan if softmax else fa.fa_moments_scan
-        ms = time_launches(lambda: sfn(xd, sa, sb), max(3, steps // 2), max(2, warmup // 2),
+        # through the workspace entry point: rows of 2 to 64 whole 2048-element blocks
+        # are shared by several workgroups (the clearing of the workspace included)
+        ws = torch.empty(max(fa.fa_scan_workspace_bytes(w.rows, w.n, xd.dtype), 8), dtype=torch.uint8,
+                         device="cuda")
+        sfn = fa.fa_softmax_scan_ws if softmax else fa.fa_moments_scan_ws
+        ms = time_launches(lambda: sfn(xd, sa, sb, ws), max(3, steps // 2), max(2, warmup // 2),
                            torch)
+        rfn = fa.fa_softmax_scan if softmax else fa.fa_moments_scan
+        ms_row = time_launches(lambda: rfn(xd, sa, sb), max(3, steps // 2), max(2, warmup // 2),
+                               torch)
         nbytes = w.bytes_read() + 2 * 4 * w.rows * w.n
         gbs = nbytes / (ms * 1e-3) / 1e9
         skernel = "row_scan_kernel<" + ("SoftmaxMonoid" if softmax else "WelfordMonoid") + ">"
         rs = {"workload": name, "op": "inclusive scan", "ms": ms, "value": gbs, "unit": "GB/s",
+              "workspace_bytes": int(fa.fa_scan_workspace_bytes(w.rows, w.n, xd.dtype)),
+              "one_workgroup_per_row": {"ms": ms_row, "gbs": nbytes / (ms_row * 1e-3) / 1e9},
               "roofline": {"kernel": skernel, "bound": "hbm", "achieved": gbs,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                            "traffic": measured_traffic(skernel, name),
                            "algorithmic_bytes_per_launch": nbytes,
                            "read_bytes": w.bytes_read(), "write_bytes": 2 * 4 * w.rows * w.n}}
         res.append(rs)
-        del x, xd, sa, sb
+        del x, xd, sa, sb, ws
         torch.cuda.empty_cache()
     return res
 

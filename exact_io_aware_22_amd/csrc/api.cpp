@@ -42,7 +42,7 @@ const char* fa_strerror(int code) {
     case FA_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte, m/d/lse/delta 4-byte alignment)";
     case FA_ERR_ARG: return "invalid argument: scale must be finite and > 0, causal 0 or 1, windows >= -1";
     case FA_ERR_HIP: return "the HIP runtime rejected the kernel launch";
-    case FA_ERR_SCRATCH: return "fa_decode_noalloc: the partial states exceed the library's static scratch (2*ceil64(B*H*splits) + B*H*splits*D > FA_DECODE_SCRATCH_FLOATS floats)";
+    case FA_ERR_SCRATCH: return "scratch too small: fa_decode_noalloc's partial states exceed the library's static scratch (2*ceil64(B*H*splits) + B*H*splits*D > FA_DECODE_SCRATCH_FLOATS floats), or a scan's workspace is smaller than fa_scan_workspace_bytes";
     default: return "unknown fa error code";
   }
 }
@@ -213,6 +213,58 @@ int fa_softmax_scan(const void* x, float* m, float* d, int rows, int n, int dtyp
 int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int dtype,
                     void* stream) {
   return row_scan(x, mean, m2, rows, n, dtype, stream, fa::launch_moments_scan);
+}
+
+long long fa_scan_workspace_bytes(int rows, int n, int dtype) {
+  if (rows < 0 || n < 0 || !count_ok(rows, n, 2, 1)) return -1;
+  if (dtype != FA_F32 && dtype != FA_BF16) return -1;
+  return fa::scan_workspace_bytes(rows, n, dtype == FA_BF16);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scans with a workspace: the same validation, then the workspace of the chained
+// path (needed only when fa_scan_workspace_bytes is not 0).
+int row_scan_ws(const void* x, float* out0, float* out1, int rows, int n, int dtype,
+                void* workspace, long long workspace_bytes, int max_polls, void* stream,
+                hipError_t (*launch)(const fa::RowReduceArgs&, hipStream_t)) {
+  if (rows < 0 || n < 0 || !count_ok(rows, n, 2, 1)) return FA_ERR_SHAPE;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (max_polls < 0) return FA_ERR_ARG;
+  if (rows == 0 || n == 0) return FA_OK;  // empty: no pointer is touched
+  if (!x || !out0 || !out1) return FA_ERR_NULL;
+  if (!aligned(x, dtype == FA_BF16 ? 2 : 4) || !aligned(out0, 4) || !aligned(out1, 4))
+    return FA_ERR_ALIGN;
+  const int64_t need = fa::scan_workspace_bytes(rows, n, dtype == FA_BF16);
+  fa::RowReduceArgs a{x, rows, n, dtype == FA_BF16, out0, out1};
+  if (need > 0) {
+    if (!workspace) return FA_ERR_NULL;
+    if (!aligned(workspace, 8)) return FA_ERR_ALIGN;
+    if (workspace_bytes < need) return FA_ERR_SCRATCH;
+    a.slots = static_cast<uint64_t*>(workspace);
+    a.max_polls = max_polls;
+  }
+  return hip_status(launch(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_softmax_scan_ws(const void* x, float* m, float* d, int rows, int n, int dtype,
+                       void* workspace, long long workspace_bytes, int max_polls,
+                       void* stream) {
+  return row_scan_ws(x, m, d, rows, n, dtype, workspace, workspace_bytes, max_polls, stream,
+                     fa::launch_softmax_scan);
+}
+
+int fa_moments_scan_ws(const void* x, float* mean, float* m2, int rows, int n, int dtype,
+                       void* workspace, long long workspace_bytes, int max_polls,
+                       void* stream) {
+  return row_scan_ws(x, mean, m2, rows, n, dtype, workspace, workspace_bytes, max_polls,
+                     stream, fa::launch_moments_scan);
 }
 
 }  // extern "C"

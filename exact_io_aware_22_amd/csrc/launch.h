@@ -65,6 +65,8 @@ struct RowReduceArgs {
   bool bf16;
   float* out0;  // softmax: m; moments: mean ([rows], or [rows][n] for a scan)
   float* out1;  // softmax: d; moments: M2
+  uint64_t* slots = nullptr;  // scans: workspace of the chained path (null: one row per workgroup)
+  int max_polls = 0;          // scans: polls before a block is folded locally (0: default)
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
@@ -86,6 +88,12 @@ hipError_t launch_moments(const RowReduceArgs& a, hipStream_t s);
 // Inclusive scans: out0, out1 are [rows][n].
 hipError_t launch_softmax_scan(const RowReduceArgs& a, hipStream_t s);
 hipError_t launch_moments_scan(const RowReduceArgs& a, hipStream_t s);
+// Chained scans: rows of more than 32 KB of input whose length is a multiple of 2048
+// elements with 2 to 64 such blocks are cut into blocks, one workgroup each (given a
+// workspace and aligned tensors); the block count, or 0 when a row takes one workgroup.
+int scan_chain_blocks(int n, bool bf16);
+// Workspace bytes the chained scans need for rows x n (0 when they do not apply).
+int64_t scan_workspace_bytes(int64_t rows, int n, bool bf16);
 
 hipError_t launch_calibrate_mfma(float* out, int blocks, int iters, uint32_t seed, hipStream_t s);
 hipError_t launch_calibrate_overlap(float* out, int blocks, int iters, int mode,

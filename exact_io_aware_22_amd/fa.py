@@ -25,7 +25,8 @@ FA_F32, FA_BF16 = 0, 1
 _DTYPES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}
 EXPORTED = ("fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
             "fa_decode_noalloc", "fa_backward", "fa_softmax_stats", "fa_moments",
-            "fa_softmax_scan", "fa_moments_scan", "fa_calibrate_mfma", "fa_calibrate_overlap",
+            "fa_softmax_scan", "fa_moments_scan", "fa_softmax_scan_ws", "fa_moments_scan_ws",
+            "fa_scan_workspace_bytes", "fa_calibrate_mfma", "fa_calibrate_overlap",
             "fa_calibrate_read", "fa_calibrate_write", "fa_calibrate_mix", "fa_strerror",
             "fa_abi_version")
 
@@ -56,6 +57,11 @@ def load():
     for name in ("fa_softmax_scan", "fa_moments_scan"):
         getattr(lib, name).argtypes = [vp, vp, vp, i, i, i, vp]
         getattr(lib, name).restype = i
+    for name in ("fa_softmax_scan_ws", "fa_moments_scan_ws"):
+        getattr(lib, name).argtypes = [vp, vp, vp, i, i, i, vp, ctypes.c_longlong, i, vp]
+        getattr(lib, name).restype = i
+    lib.fa_scan_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_scan_workspace_bytes.restype = ctypes.c_longlong
     lib.fa_decode_partials.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_decode_partials.restype = i
     lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
@@ -337,6 +343,44 @@ def fa_moments_scan(x, mean, m2, stream=None) -> None:
     _check(code, "fa_moments_scan")
 
 
+def fa_scan_workspace_bytes(rows: int, n: int, dtype=torch.float32) -> int:
+    """Workspace bytes fa_softmax_scan_ws / fa_moments_scan_ws need for rows x n elements
+    of dtype (a torch dtype)."""
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}; expected float32 or bfloat16")
+    nbytes = load().fa_scan_workspace_bytes(int(rows), int(n), _DTYPES[dtype])
+    if nbytes < 0:
+        raise ValueError(f"invalid scan size rows={rows} n={n}")
+    return int(nbytes)
+
+
+def _scan_ws(name, x, out0, out1, workspace, max_polls, stream):
+    rows, n = _scan_shapes(x, out0, out1)
+    need = fa_scan_workspace_bytes(rows, n, x.dtype)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _want_dtype("workspace", workspace, torch.uint8)
+        _dense(workspace)
+        _on_one_device(x=x, workspace=workspace)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    if ws_bytes < need:
+        raise ValueError(f"workspace must hold {need} bytes, got {ws_bytes}")
+    code = getattr(load(), name)(_ptr(x), _ptr(out0), _ptr(out1), rows, n, _dtype_code(x),
+                                 ws_ptr, ws_bytes, int(max_polls), _stream(stream))
+    _check(code, name)
+
+
+def fa_softmax_scan_ws(x, m, d, workspace, max_polls: int = 0, stream=None) -> None:
+    """fa_softmax_scan with a uint8 device workspace of fa_scan_workspace_bytes bytes, which
+    lets several workgroups share a row (see include/fa.h)."""
+    _scan_ws("fa_softmax_scan_ws", x, m, d, workspace, max_polls, stream)
+
+
+def fa_moments_scan_ws(x, mean, m2, workspace, max_polls: int = 0, stream=None) -> None:
+    """fa_moments_scan with a workspace, as fa_softmax_scan_ws."""
+    _scan_ws("fa_moments_scan_ws", x, mean, m2, workspace, max_polls, stream)
+
+
 def fa_calibrate_mfma(out, blocks: int, iters: int, seed: int = 0, stream=None) -> None:
     """Measurement only: the MFMA-only loop; out: fp32 [blocks * 512] (checksums).
     One launch is 2**19 * 8 * blocks * iters flops."""
@@ -409,19 +453,25 @@ def softmax_stats(x, stream=None):
     return m, d
 
 
+def _workspace_for(x):
+    rows = math.prod(x.shape[:-1]) if x.dim() > 0 else 0
+    need = fa_scan_workspace_bytes(rows, x.shape[-1], x.dtype) if x.dim() > 0 else 0
+    return torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+
+
 def softmax_scan(x, stream=None):
-    """Allocate m, d (x's shape, fp32) and run fa_softmax_scan."""
+    """Allocate m, d (x's shape, fp32) and a workspace, and run fa_softmax_scan_ws."""
     m = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     d = torch.empty_like(m)
-    fa_softmax_scan(x, m, d, stream)
+    fa_softmax_scan_ws(x, m, d, _workspace_for(x), 0, stream)
     return m, d
 
 
 def moments_scan(x, stream=None):
-    """Allocate mean, m2 (x's shape, fp32) and run fa_moments_scan."""
+    """Allocate mean, m2 (x's shape, fp32) and a workspace, and run fa_moments_scan_ws."""
     mean = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     m2 = torch.empty_like(mean)
-    fa_moments_scan(x, mean, m2, stream)
+    fa_moments_scan_ws(x, mean, m2, _workspace_for(x), 0, stream)
     return mean, m2
 
 

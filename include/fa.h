@@ -57,7 +57,8 @@ enum {
                         bound below -1 (numbered after FA_ERR_HIP so the first five
                         codes keep the values of the original five-code interface) */
   FA_ERR_SCRATCH = -7 /* fa_decode_noalloc: the partial states need more than the
-                         library's static scratch (FA_DECODE_SCRATCH_FLOATS)         */
+                         library's static scratch (FA_DECODE_SCRATCH_FLOATS); a _ws
+                         scan: the workspace is smaller than fa_scan_workspace_bytes */
 };
 
 /* Capacity, in floats, of the static device array fa_decode_noalloc keeps its
@@ -254,6 +255,37 @@ int fa_softmax_scan(const void* x, float* m, float* d, int rows, int n, int dtyp
                     void* stream);
 int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int dtype,
                     void* stream);
+
+/*
+ * fa_softmax_scan_ws, fa_moments_scan_ws -- the same scans, with a caller workspace that
+ * lets one row be shared by several workgroups. A row of more than 32 KB of input whose
+ * length n is a multiple of 2048 with 2 to 64 such blocks is cut into its 2048-element
+ * blocks, one workgroup each: block k publishes the fold of its own elements and starts
+ * from the fold of blocks 0 .. k-1 (the prefix of a monoid can be bracketed at any block
+ * boundary, section "Associativity is All You Need"). Other rows, or tensors not
+ * 16-byte aligned, take the one-workgroup-per-row path of fa_softmax_scan /
+ * fa_moments_scan and leave the workspace untouched.
+ *   workspace       : device memory of at least fa_scan_workspace_bytes(rows, n) bytes,
+ *                     8-byte aligned, owned by the caller; may be NULL when that size is
+ *                     0. The call clears and rewrites it (its contents on return mean
+ *                     nothing); calls that overlap in time need separate workspaces.
+ *   workspace_bytes : its size; smaller than needed returns FA_ERR_SCRATCH.
+ *   max_polls       : how many times a block polls for an earlier block's published
+ *                     fold before folding that block's elements itself (0: 65536; a
+ *                     negative value returns FA_ERR_ARG). Every wait is bounded by it.
+ * Results agree with fa_softmax_scan / fa_moments_scan to rounding (the folds are
+ * bracketed differently), not bit for bit.
+ */
+int fa_softmax_scan_ws(const void* x, float* m, float* d, int rows, int n, int dtype,
+                       void* workspace, long long workspace_bytes, int max_polls,
+                       void* stream);
+int fa_moments_scan_ws(const void* x, float* mean, float* m2, int rows, int n, int dtype,
+                       void* workspace, long long workspace_bytes, int max_polls,
+                       void* stream);
+/* Workspace bytes the _ws scans need for rows x n elements of dtype: 8 per 2048-element
+ * block when a row of more than 32 KB has 2 to 64 whole blocks, else 0; -1 for negative
+ * or oversized sizes or an unknown dtype. */
+long long fa_scan_workspace_bytes(int rows, int n, int dtype);
 
 /*
  * Measurement calls. They compute nothing of the method: they measure the chip's

@@ -81,6 +81,16 @@ int64_t decode_noalloc_floats(int64_t units, int D) {
   return 2 * ((units + 63) / 64 * 64) + units * D;
 }
 
+// The chained scans' rule as the header states it: 8 bytes per 2048-element block when a
+// row of more than 32 KB has 2 to 64 whole blocks.
+int scan_chain_blocks(int n, bool bf16) {
+  if (n <= 0 || n % 2048 != 0 || int64_t(n) * (bf16 ? 2 : 4) <= 32768) return 0;
+  return n / 2048 >= 2 && n / 2048 <= 64 ? n / 2048 : 0;
+}
+int64_t scan_workspace_bytes(int64_t rows, int n, bool bf16) {
+  return rows * scan_chain_blocks(n, bf16) * 8;
+}
+
 static void check_fwd(const FwdArgs& a) {
   CHECK(a.B > 0 && a.H > 0 && a.N > 0 && (a.D == 64 || a.D == 128));
   CHECK(al(a.q, 16) && al(a.k, 16) && al(a.v, 16) && al(a.o, 16) && al(a.lse, 4));
@@ -161,6 +171,9 @@ static void check_rows(const RowReduceArgs& a, bool scan) {
   if (scan) CHECK(a.n > 0 && prod({(long double)a.rows, (long double)a.n, 2.0L}) < kLimit);
   if (a.n > 0) CHECK(al(a.x, a.bf16 ? 2 : 4));
   CHECK(al(a.out0, 4) && al(a.out1, 4));
+  // a workspace is passed exactly when the chained path applies by size, aligned
+  CHECK(a.max_polls >= 0);
+  if (a.slots) CHECK(scan && scan_chain_blocks(a.n, a.bf16) > 0 && al(a.slots, 8));
 }
 hipError_t launch_softmax_stats(const RowReduceArgs& a, hipStream_t) {
   record("softmax_stats");
@@ -472,6 +485,15 @@ void sweep(int iterations) {
     sweep_call(7, "fa_moments", [&] { return fa_moments(pick_ptr(), pick_fptr(), pick_fptr(), rows, n, dt, nullptr); });
     sweep_call(8, "fa_softmax_scan", [&] { return fa_softmax_scan(pick_ptr(), pick_fptr(), pick_fptr(), rows, n, dt, nullptr); });
     sweep_call(9, "fa_moments_scan", [&] { return fa_moments_scan(pick_ptr(), pick_fptr(), pick_fptr(), rows, n, dt, nullptr); });
+    const int polls = pick_int();
+    sweep_call(15, "fa_softmax_scan_ws", [&] { return fa_softmax_scan_ws(pick_ptr(), pick_fptr(), pick_fptr(), rows, n, dt,
+                                        pick_ptr(), nb, polls, nullptr); });
+    sweep_call(16, "fa_moments_scan_ws", [&] { return fa_moments_scan_ws(pick_ptr(), pick_fptr(), pick_fptr(), rows, n, dt,
+                                        pick_ptr(), nb, polls, nullptr); });
+    {
+      const long long w = fa_scan_workspace_bytes(rows, n, dt);
+      CHECK(w == -1 || w == int64_t(rows) * fa::scan_chain_blocks(n, dt == 1) * 8);
+    }
     sweep_call(10, "fa_calibrate_mfma", [&] { return fa_calibrate_mfma(pick_fptr(), blocks, iters, unsigned(it), nullptr); });
     sweep_call(11, "fa_calibrate_overlap", [&] { return fa_calibrate_overlap(pick_fptr(), blocks, iters, mode, nullptr); });
     sweep_call(12, "fa_calibrate_read", [&] { return fa_calibrate_read(pick_ptr(), nb, static_cast<unsigned*>(pick_ptr()), blocks,

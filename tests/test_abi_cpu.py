@@ -38,6 +38,7 @@ def test_header_declares_the_documented_calls():
         ["fa_forward", "fa_forward_ext", "fa_decode_partials", "fa_combine_partials",
          "fa_decode_noalloc",
          "fa_backward", "fa_softmax_stats", "fa_moments", "fa_softmax_scan", "fa_moments_scan",
+         "fa_softmax_scan_ws", "fa_moments_scan_ws", "fa_scan_workspace_bytes",
          "fa_calibrate_mfma", "fa_calibrate_overlap", "fa_calibrate_read", "fa_calibrate_write", "fa_calibrate_mix",
          "fa_strerror", "fa_abi_version"])
 
@@ -208,6 +209,42 @@ def test_row_scan_validation(lib, which):
     assert red(lib, which, rows=0, x=None, o0=None, o1=None) == OK  # empty
     assert red(lib, which, n=0, x=None, o0=None, o1=None) == OK     # empty rows
     assert red(lib, which, rows=1 << 30, n=1 << 30) == SHAPE         # offsets overflow
+
+
+def test_scan_workspace_bytes(lib):
+    f = lib.fa_scan_workspace_bytes
+    F32, BF16 = 0, 1
+    assert f(8192, 32768, F32) == 8192 * 16 * 8  # 16 blocks of 2048 per 128 KB row
+    assert f(65536, 8192, BF16) == 0             # 16 KB rows: one workgroup each
+    assert f(3, 5 * 2048, F32) == 3 * 5 * 8      # 40 KB rows: cut
+    assert f(3, 4 * 2048, F32) == 0              # 32 KB rows: not
+    assert f(3, 9 * 2048, BF16) == 3 * 9 * 8
+    assert f(3, 8 * 2048, BF16) == 0
+    assert f(3, 64 * 2048, BF16) == 3 * 64 * 8   # the most blocks that are cut
+    for n in (0, 1, 2047, 2048, 6000, 65 * 2048, 20000):
+        assert f(5, n, F32) == 0, n              # one workgroup per row
+    assert f(0, 32768, F32) == 0
+    assert f(-1, 4096, F32) == -1 and f(5, -1, F32) == -1 and f(5, 32768, 7) == -1
+    assert f(1 << 30, 1 << 30, F32) == -1        # offsets overflow
+
+
+@pytest.mark.parametrize("which", ["fa_softmax_scan_ws", "fa_moments_scan_ws"])
+def test_row_scan_ws_validation(lib, which):
+    fn = getattr(lib, which)
+
+    def call(x=P, o0=P, o1=P, rows=4, n=32768, dtype=1, ws=P, nbytes=4 * 16 * 8, polls=0):
+        return fn(x, o0, o1, rows, n, dtype, ws, nbytes, polls, None)
+
+    assert call(x=None) == NULL
+    assert call(ws=None) == NULL                  # 16 blocks per row: the workspace is needed
+    assert call(nbytes=4 * 16 * 8 - 1) == SCRATCH
+    assert call(ws=P + 4) == ALIGN
+    assert call(polls=-1) == ARG
+    assert call(rows=-1) == SHAPE
+    assert call(dtype=7) == DTYPE
+    assert call(x=P + 1) == ALIGN
+    assert call(rows=0, x=None, o0=None, o1=None, ws=None, nbytes=0) == OK  # empty
+    assert call(n=0, x=None, o0=None, o1=None, ws=None, nbytes=0) == OK     # empty rows
 
 
 def test_calibration_validation(lib):

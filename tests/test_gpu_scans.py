@@ -102,6 +102,71 @@ def test_moments_scan(dtype, n, offset):
     check_moments_scan(x, mean, m2, f"moments_scan n={n} off={offset}")
 
 
+def run_ws(fn, x, offset=0, max_polls=0, workspace=None):
+    """As run(), through the workspace entry point (several workgroups per row when the
+    row has 2 to 64 whole 2048-element blocks and the tensors are aligned)."""
+    rows, n = x.shape
+    buf = torch.full((rows * n + offset + 8,), float("nan"), dtype=x.dtype, device="cuda")
+    xd = buf[offset:offset + rows * n].view(rows, n)
+    xd.copy_(x.cuda())
+    outs = [torch.full((rows * n + offset + 8,), float("nan"), device="cuda") for _ in range(2)]
+    a, b = (o[offset:offset + rows * n].view(rows, n) for o in outs)
+    if workspace is None:
+        workspace = torch.empty(max(fa.fa_scan_workspace_bytes(rows, n, x.dtype), 8), dtype=torch.uint8,
+                                device="cuda")
+    fn(xd, a, b, workspace, max_polls)
+    torch.cuda.synchronize()
+    return a.cpu().double().numpy(), b.cpu().double().numpy()
+
+
+# Rows of more than 32 KB with 2 to 64 whole blocks take the chained path when aligned
+# (float32: 5 blocks and up; bfloat16: 9 and up); shorter rows, 65 blocks, a ragged
+# length or an unaligned row take the one-workgroup-per-row path.
+CHAIN_CASES = [(torch.float32, 5 * 2048, 3), (torch.float32, 16384, 2), (torch.float32, 32768, 1),
+               (torch.float32, 8192, 3), (torch.bfloat16, 9 * 2048, 2),
+               (torch.bfloat16, 32768, 1), (torch.bfloat16, 16384, 2),
+               (torch.float32, 20000, 2)]
+
+
+@pytest.mark.parametrize("dtype,n,rows", CHAIN_CASES,
+                         ids=[f"{'bf16' if d == torch.bfloat16 else 'fp32'}-{n}" for d, n, _ in CHAIN_CASES])
+@pytest.mark.parametrize("offset", [0, 3])
+def test_chained_scans(dtype, n, rows, offset):
+    say(f"chained scans n={n} rows={rows} {dtype} offset={offset}")
+    x = random_tensor((rows, n), 950 + n + offset, dtype, sigma=8.0)
+    m, d = run_ws(fa.fa_softmax_scan_ws, x, offset)
+    check_softmax_scan(x, m, d, f"softmax_scan_ws n={n} off={offset}")
+    x = random_tensor((rows, n), 960 + n + offset, dtype, sigma=2.0) + 1.0
+    mean, m2 = run_ws(fa.fa_moments_scan_ws, x, offset)
+    check_moments_scan(x, mean, m2, f"moments_scan_ws n={n} off={offset}")
+
+
+@pytest.mark.parametrize("polls", [1, 2])
+def test_chained_scans_fold_late_blocks_themselves(polls):
+    """With one or two polls most blocks find some earlier block's word not yet written
+    and fold that block from its elements instead: the results stay within bounds."""
+    say(f"chained scans, max_polls={polls}")
+    for dtype, n in ((torch.float32, 16384), (torch.bfloat16, 18432)):
+        x = random_tensor((3, n), 970 + polls, dtype, sigma=8.0)
+        x[1, :3000] = -math.inf
+        m, d = run_ws(fa.fa_softmax_scan_ws, x, 0, polls)
+        check_softmax_scan(x, m, d, f"softmax_scan_ws polls={polls} {dtype}")
+        x = random_tensor((3, n), 980 + polls, dtype, sigma=2.0) + 1.0
+        mean, m2 = run_ws(fa.fa_moments_scan_ws, x, 0, polls)
+        check_moments_scan(x, mean, m2, f"moments_scan_ws polls={polls} {dtype}")
+
+
+def test_chained_scans_reuse_one_workspace():
+    """Three calls in a row share a workspace: each clears it first, so words left by the
+    previous call are never taken for this call's."""
+    ws = torch.empty(fa.fa_scan_workspace_bytes(4, 16384), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    for i in range(3):
+        x = random_tensor((4, 16384), 990 + i, torch.float32, sigma=4.0 * (i + 1))
+        m, d = run_ws(fa.fa_softmax_scan_ws, x, workspace=ws)
+        check_softmax_scan(x, m, d, f"softmax_scan_ws call {i}")
+
+
 def test_softmax_scan_leading_masked_entries():
     """-inf prefixes are the identity; the first finite entry starts d at 1."""
     x = random_tensor((3, 3000), 901, torch.float32, sigma=50.0)
@@ -128,8 +193,9 @@ def test_scans_end_in_the_reductions():
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("chained", [False, True], ids=["row_per_workgroup", "chained"])
 @pytest.mark.parametrize("name", ["moments_activations_bf16", "softmax_stats_logits_fp32"])
-def test_scan_full_size_whole_rows(name):
+def test_scan_full_size_whole_rows(name, chained):
     """The benchmark's scans at full size (the row reductions' 1 GiB inputs): every
     position of 6 whole rows (the first, the last and 4 seeded ones) against the
     oracle's reduction of each prefix, within the tolerances above; every row's last
@@ -142,8 +208,13 @@ def test_scan_full_size_whole_rows(name):
     a = torch.empty(w.rows, w.n, device="cuda")
     b = torch.empty(w.rows, w.n, device="cuda")
     softmax = name.startswith("softmax")
-    say(f"{name} scan at full size")
-    (fa.fa_softmax_scan if softmax else fa.fa_moments_scan)(xd, a, b)
+    say(f"{name} scan at full size, chained={chained}")
+    if chained:
+        ws = torch.empty(max(fa.fa_scan_workspace_bytes(w.rows, w.n, x.dtype), 8), dtype=torch.uint8,
+                         device="cuda")
+        (fa.fa_softmax_scan_ws if softmax else fa.fa_moments_scan_ws)(xd, a, b, ws)
+    else:
+        (fa.fa_softmax_scan if softmax else fa.fa_moments_scan)(xd, a, b)
     torch.cuda.synchronize()
     del xd
     rng = np.random.default_rng(6)
