@@ -31,7 +31,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 extern "C" {
 
-int fa_abi_version(void) { return 1; }
+int fa_abi_version(void) { return 2; }
 
 const char* fa_strerror(int code) {
   switch (code) {

@@ -359,7 +359,7 @@ int fa_calibrate_mix(const void* x, long long nbytes, void* y, int ratio, int bl
 /* Static, human-readable name of an FA_* code (never NULL). */
 const char* fa_strerror(int code);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (version 1 had no workspace scans). */
 int fa_abi_version(void);
 
 #ifdef __cplusplus

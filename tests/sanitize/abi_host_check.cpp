@@ -424,7 +424,7 @@ void known_answers() {
   // strerror covers every code and unknown ones
   for (int c : {0, -1, -2, -3, -4, -5, -6, -7, -8, 1, INT_MIN, INT_MAX})
     CHECK(fa_strerror(c) != nullptr && std::strlen(fa_strerror(c)) > 0);
-  CHECK(fa_abi_version() == 1);
+  CHECK(fa_abi_version() == 2);
 }
 
 // Extreme values for the sweep.

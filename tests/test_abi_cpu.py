@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
     for code in (OK, NULL, SHAPE, DTYPE, ALIGN, HIP, ARG, SCRATCH, 12345):
         msg = fa.strerror(code)
         assert isinstance(msg, str) and msg
