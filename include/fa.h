@@ -274,7 +274,10 @@ int fa_moments_scan(const void* x, float* mean, float* m2, int rows, int n, int 
  *                     fold before folding that block's elements itself (0: 65536; a
  *                     negative value returns FA_ERR_ARG). Every wait is bounded by it.
  * Results agree with fa_softmax_scan / fa_moments_scan to rounding (the folds are
- * bracketed differently), not bit for bit.
+ * bracketed differently), not bit for bit. Two calls on the same input give the same
+ * bits unless a block ran out of polls in one of them (it then folds the late block
+ * itself, bracketed differently again); at the default bound that takes a wait of tens
+ * of milliseconds.
  */
 int fa_softmax_scan_ws(const void* x, float* m, float* d, int rows, int n, int dtype,
                        void* workspace, long long workspace_bytes, int max_polls,

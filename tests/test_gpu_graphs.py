@@ -1,10 +1,12 @@
 """The entry points under HIP graph capture, the use the allocation-free decode is for:
-fa_forward, fa_backward and fa_decode_noalloc recorded into one graph (torch.cuda.graph
+fa_forward, fa_backward, fa_decode_noalloc and the chained scan fa_softmax_scan_ws (its
+workspace cleared by a kernel of its own) recorded into one graph (torch.cuda.graph
 captures the stream the binding launches on), then replayed several times with new
 inputs copied into the captured tensors and eager work of the same calls in between.
 
-Every kernel here is deterministic (no atomics, a fixed reduction order), so each
-replay must reproduce the eager calls on the same inputs bit for bit; the eager calls
+Every kernel here is deterministic (a fixed reduction order; the scan's blocks find their
+predecessors' words long before their bound of polls runs out), so each replay must
+reproduce the eager calls on the same inputs bit for bit; the eager calls
 are themselves compared with the oracle by the parity tests. The library records no
 memset and allocates nothing, so nothing else needs to stay out of the graph.
 """
@@ -20,6 +22,7 @@ pytestmark = pytest.mark.gpu
 
 B, H, N, D = 2, 4, 777, 128
 L, SPLITS = 3001, 16
+SCAN_N = 32768  # float32 rows of 128 KB: the chained scan (16 blocks per row)
 SCALE = 1.0 / math.sqrt(D)
 
 
@@ -37,6 +40,7 @@ def fresh_inputs(seed):
         "q1": random_tensor((B, H, 1, D), seed + 4, torch.bfloat16),
         "kc": random_tensor((B, H, L, D), seed + 5, torch.bfloat16, sigma=2.0),
         "vc": random_tensor((B, H, L, D), seed + 6, torch.bfloat16),
+        "rows": random_tensor((8, SCAN_N), seed + 7, torch.float32, sigma=8.0),
     }
 
 
@@ -51,16 +55,22 @@ def outputs():
         "dv": torch.full((B, H, N, D), float("nan"), **f32),
         "od": torch.full((B * H, D), float("nan"), **f32),
         "lsed": torch.full((B * H,), float("nan"), **f32),
+        "sm": torch.full((8, SCAN_N), float("nan"), **f32),
+        "sd": torch.full((8, SCAN_N), float("nan"), **f32),
+        # the chained scan's workspace (cleared by the call itself, so it is an output)
+        "ws": torch.zeros(fa.fa_scan_workspace_bytes(8, SCAN_N), dtype=torch.uint8,
+                          device="cuda"),
     }
 
 
 def calls(x, y):
-    """One training step's attention (forward, then backward from its o and lse) and
-    one decode step, all on the current stream."""
+    """One training step's attention (forward, then backward from its o and lse), one
+    decode step and one chained scan, all on the current stream."""
     fa.fa_forward(x["q"], x["k"], x["v"], y["o"], y["lse"], SCALE, True)
     fa.fa_backward(x["q"], x["k"], x["v"], y["o"], y["lse"], x["do"], y["delta"], y["dq"],
                    y["dk"], y["dv"], SCALE, True)
     fa.fa_decode_noalloc(x["q1"], x["kc"], x["vc"], y["od"], y["lsed"], SCALE, SPLITS)
+    fa.fa_softmax_scan_ws(x["rows"], y["sm"], y["sd"], y["ws"])
 
 
 def test_captured_calls_replay_like_eager_calls():
@@ -89,6 +99,8 @@ def test_captured_calls_replay_like_eager_calls():
         calls(eager_in, eager_out)
         torch.cuda.synchronize()
         for name in static_out:
+            if name == "ws":
+                continue  # scratch: its contents after a call mean nothing
             got, want = static_out[name], eager_out[name]
             assert bool(torch.isfinite(want).all()), f"replay {replay}: eager {name} not finite"
             assert torch.equal(got, want), (
